@@ -1,0 +1,274 @@
+// The C ABI of libgdn (include/gdn.h): host-side validation, workspace
+// carving and dispatch to the HIP kernels.  Nothing here allocates, frees or
+// synchronises; every check runs before the first launch, so a refused call
+// writes nothing.
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+
+#include <exception>
+#include <string>
+
+#include "gdn.h"
+#include "gdn_internal.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+gdn_status fail(gdn_status st, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = std::string(gdn_status_string(st)) + ": " + buf;
+  return st;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Span {
+  uintptr_t lo = 0, hi = 0;  // [lo, hi)
+  Span() = default;
+  Span(const void *p, size_t bytes) : lo(reinterpret_cast<uintptr_t>(p)), hi(lo + bytes) {}
+  bool empty() const { return lo == hi || lo == 0; }
+  bool overlaps(const Span &o) const { return !empty() && !o.empty() && lo < o.hi && o.lo < hi; }
+};
+
+size_t esize(int dt) { return dt == GDN_BF16 ? 2 : 4; }
+
+// Shape checks shared by every entry point; fills p.
+gdn_status check_shape(const gdn_shape *s, bool packed, int32_t num_seqs, bool step, gdn::Problem &p) {
+  if (!s) return fail(GDN_ERR_NULL, "shape is NULL");
+  if (s->dtype != GDN_F32 && s->dtype != GDN_BF16) return fail(GDN_ERR_DTYPE, "dtype %d", s->dtype);
+  if (s->o_dtype != GDN_F32 && s->o_dtype != GDN_BF16) return fail(GDN_ERR_DTYPE, "o_dtype %d", s->o_dtype);
+  if (s->B < 0 || s->T < 0) return fail(GDN_ERR_SHAPE, "B=%d T=%d", s->B, s->T);
+  if (s->H_qk <= 0 || s->H_v <= 0 || s->H_v % s->H_qk != 0)
+    return fail(GDN_ERR_SHAPE, "H_qk=%d H_v=%d (H_v must be a positive multiple of H_qk)", s->H_qk, s->H_v);
+  if (s->d_k <= 0 || s->d_v <= 0) return fail(GDN_ERR_SHAPE, "d_k=%d d_v=%d", s->d_k, s->d_v);
+  if (s->flags & ~(uint32_t)GDN_QK_L2NORM) return fail(GDN_ERR_SHAPE, "unknown flags 0x%x", s->flags);
+  if (!(s->scale == s->scale)) return fail(GDN_ERR_SHAPE, "scale is NaN");
+  if (step) {
+    if (s->T != 1) return fail(GDN_ERR_SHAPE, "the decode step takes T == 1, got %d", s->T);
+  } else if (s->chunk <= 0) {
+    return fail(GDN_ERR_SHAPE, "chunk=%d", s->chunk);
+  }
+  if (packed) {
+    if (s->B != 1) return fail(GDN_ERR_SHAPE, "packed sequences need B == 1, got %d", s->B);
+    if (num_seqs < 0) return fail(GDN_ERR_SHAPE, "num_seqs=%d", num_seqs);
+  }
+  const int64_t T_tot = (int64_t)s->B * s->T;
+  // Every flat index a kernel forms must fit comfortably (token counts in int32).
+  if (T_tot > (1LL << 30)) return fail(GDN_ERR_SHAPE, "B*T=%lld too large", (long long)T_tot);
+  p.B = s->B;
+  p.T = s->T;
+  p.H_qk = s->H_qk;
+  p.H_v = s->H_v;
+  p.d_k = s->d_k;
+  p.d_v = s->d_v;
+  p.C = step ? 1 : s->chunk;
+  p.packed = packed;
+  p.N = packed ? num_seqs : s->B;
+  p.T_tot = (int)T_tot;
+  p.scale = s->scale;
+  p.dtype = s->dtype;
+  p.o_dtype = s->o_dtype;
+  p.l2norm = (s->flags & GDN_QK_L2NORM) != 0;
+  p.max_chunks = 0;
+  if (!step) {
+    const int64_t mc = packed ? (T_tot + p.C - 1) / p.C + p.N : (int64_t)p.B * ((p.T + p.C - 1) / p.C);
+    if (mc * p.H_v > (1LL << 30)) return fail(GDN_ERR_SHAPE, "too many chunks");
+    p.max_chunks = (int)mc;
+  }
+  return GDN_OK;
+}
+
+struct Tensors {
+  Span q, k, v, g, beta, s0, cu, o, states, fin, ws;
+};
+
+Tensors spans(const gdn::Problem &p, const void *q, const void *k, const void *v, const float *g,
+              const float *beta, const float *s0, const int32_t *cu, const void *o, const float *states,
+              const float *fin, const void *ws, size_t ws_bytes) {
+  const size_t T = p.T_tot, es = esize(p.dtype);
+  const size_t state_bytes = (size_t)p.N * p.H_v * p.d_k * p.d_v * sizeof(float);
+  Tensors t;
+  t.q = Span(q, T * p.H_qk * p.d_k * es);
+  t.k = Span(k, T * p.H_qk * p.d_k * es);
+  t.v = Span(v, T * p.H_v * p.d_v * es);
+  t.g = Span(g, T * p.H_v * sizeof(float));
+  t.beta = Span(beta, T * p.H_v * sizeof(float));
+  t.s0 = Span(s0, state_bytes);
+  t.cu = Span(cu, ((size_t)p.N + 1) * sizeof(int32_t));
+  t.o = Span(o, T * p.H_v * p.d_v * esize(p.o_dtype));
+  t.states = Span(states, T * p.H_v * p.d_k * p.d_v * sizeof(float));
+  t.fin = Span(fin, state_bytes);
+  t.ws = Span(ws, ws_bytes);
+  return t;
+}
+
+gdn_status chunked_common(const gdn_shape *s, const void *q, const void *k, const void *v, const float *g,
+                          const float *beta, const float *initial_state, const int32_t *cu_seqlens,
+                          int32_t num_seqs, void *o, float *states, float *final_state, void *workspace,
+                          size_t workspace_bytes, hipStream_t stream, bool with_states) {
+  gdn::Problem p;
+  gdn_status st = check_shape(s, cu_seqlens != nullptr, num_seqs, false, p);
+  if (st != GDN_OK) return st;
+  if (!gdn::chunk_path_supported(p))
+    return fail(GDN_ERR_UNSUPPORTED, "no chunked kernel for dtype=%d d_k=%d d_v=%d chunk=%d", p.dtype, p.d_k,
+                p.d_v, p.C);
+  const bool any_tokens = p.T_tot > 0;
+  if (any_tokens && (!q || !k || !v || !g || !beta)) return fail(GDN_ERR_NULL, "q, k, v, g and beta are required");
+  if (!with_states && any_tokens && !o) return fail(GDN_ERR_NULL, "o is required");
+  if (with_states && any_tokens && !states) return fail(GDN_ERR_NULL, "states is required");
+  const gdn::Workspace need = gdn::workspace_layout(p, with_states, nullptr);
+  if (!workspace) return fail(GDN_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need.bytes);
+  if (workspace_bytes < need.bytes)
+    return fail(GDN_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, need.bytes);
+  const void *ptrs[] = {q, k, v, g, beta, initial_state, o, states, final_state, workspace};
+  const char *names[] = {"q", "k", "v", "g", "beta", "initial_state", "o", "states", "final_state", "workspace"};
+  for (int i = 0; i < 10; ++i)
+    if (ptrs[i] && !aligned16(ptrs[i])) return fail(GDN_ERR_ALIGN, "%s is not 16-byte aligned", names[i]);
+  if (cu_seqlens && (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u)) return fail(GDN_ERR_ALIGN, "cu_seqlens");
+
+  const Tensors t = spans(p, q, k, v, g, beta, initial_state, cu_seqlens, o, states, final_state, workspace,
+                          workspace_bytes);
+  const Span ins[] = {t.q, t.k, t.v, t.g, t.beta, t.s0, t.cu};
+  const char *in_names[] = {"q", "k", "v", "g", "beta", "initial_state", "cu_seqlens"};
+  struct Out {
+    Span s;
+    const char *name;
+  } outs[] = {{t.o, "o"}, {t.states, "states"}, {t.fin, "final_state"}, {t.ws, "workspace"}};
+  for (const Out &x : outs) {
+    for (int i = 0; i < 7; ++i) {
+      if (!x.s.overlaps(ins[i])) continue;
+      // The one permitted overlap: final_state == initial_state exactly.
+      const bool inplace = (&x == &outs[2]) && i == 5 && x.s.lo == ins[i].lo && x.s.hi == ins[i].hi;
+      if (!inplace) return fail(GDN_ERR_ALIAS, "%s overlaps %s", x.name, in_names[i]);
+    }
+  }
+  for (int a = 0; a < 4; ++a)
+    for (int b = a + 1; b < 4; ++b)
+      if (outs[a].s.overlaps(outs[b].s)) return fail(GDN_ERR_ALIAS, "%s overlaps %s", outs[a].name, outs[b].name);
+
+  gdn::ChunkArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.g = g;
+  a.beta = beta;
+  a.s0 = initial_state;
+  a.cu = cu_seqlens;
+  a.o = o;
+  a.final_state = final_state;
+  a.states = states;
+  a.ws = gdn::workspace_layout(p, with_states, workspace);
+  const hipError_t e = gdn::launch_chunk_path(p, a, with_states, stream);
+  if (e != hipSuccess) return fail(GDN_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+  g_last_error.clear();
+  return GDN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *gdn_status_string(gdn_status st) {
+  switch (st) {
+    case GDN_OK: return "GDN_OK";
+    case GDN_ERR_NULL: return "GDN_ERR_NULL";
+    case GDN_ERR_SHAPE: return "GDN_ERR_SHAPE";
+    case GDN_ERR_DTYPE: return "GDN_ERR_DTYPE";
+    case GDN_ERR_UNSUPPORTED: return "GDN_ERR_UNSUPPORTED";
+    case GDN_ERR_ALIAS: return "GDN_ERR_ALIAS";
+    case GDN_ERR_ALIGN: return "GDN_ERR_ALIGN";
+    case GDN_ERR_WORKSPACE: return "GDN_ERR_WORKSPACE";
+    case GDN_ERR_HIP: return "GDN_ERR_HIP";
+  }
+  return "GDN_UNKNOWN_STATUS";
+}
+
+const char *gdn_last_error(void) { return g_last_error.c_str(); }
+
+int gdn_version(void) { return 100; }
+
+static size_t workspace_query(const gdn_shape *s, int32_t num_seqs, bool states) {
+  try {
+    const std::string keep = g_last_error;  // a query never changes the last error
+    gdn::Problem p;
+    const gdn_status st = check_shape(s, num_seqs > 0, num_seqs, false, p);
+    g_last_error = keep;
+    if (st != GDN_OK) return 0;
+    return gdn::workspace_layout(p, states, nullptr).bytes;
+  } catch (...) {
+    return 0;
+  }
+}
+
+size_t gdn_chunk_fwd_workspace(const gdn_shape *s, int32_t num_seqs) { return workspace_query(s, num_seqs, false); }
+
+size_t gdn_states_fwd_workspace(const gdn_shape *s, int32_t num_seqs) { return workspace_query(s, num_seqs, true); }
+
+gdn_status gdn_chunk_fwd(const gdn_shape *s, const void *q, const void *k, const void *v, const float *g,
+                         const float *beta, const float *initial_state, const int32_t *cu_seqlens,
+                         int32_t num_seqs, void *o, float *final_state, void *workspace, size_t workspace_bytes,
+                         hipStream_t stream) {
+  try {
+    return chunked_common(s, q, k, v, g, beta, initial_state, cu_seqlens, num_seqs, o, nullptr, final_state,
+                          workspace, workspace_bytes, stream, false);
+  } catch (const std::exception &e) {
+    return fail(GDN_ERR_HIP, "internal error: %s", e.what());
+  } catch (...) {
+    return fail(GDN_ERR_HIP, "internal error");
+  }
+}
+
+gdn_status gdn_states_fwd(const gdn_shape *s, const void *q, const void *k, const void *v, const float *g,
+                          const float *beta, const float *initial_state, const int32_t *cu_seqlens,
+                          int32_t num_seqs, void *o, float *states, float *final_state, void *workspace,
+                          size_t workspace_bytes, hipStream_t stream) {
+  try {
+    return chunked_common(s, q, k, v, g, beta, initial_state, cu_seqlens, num_seqs, o, states, final_state,
+                          workspace, workspace_bytes, stream, true);
+  } catch (const std::exception &e) {
+    return fail(GDN_ERR_HIP, "internal error: %s", e.what());
+  } catch (...) {
+    return fail(GDN_ERR_HIP, "internal error");
+  }
+}
+
+gdn_status gdn_recurrent_step(const gdn_shape *s, const void *q, const void *k, const void *v, const float *g,
+                              const float *beta, float *state, void *o, hipStream_t stream) {
+  try {
+    gdn::Problem p;
+    gdn_status st = check_shape(s, false, 0, true, p);
+    if (st != GDN_OK) return st;
+    if (!gdn::step_supported(p))
+      return fail(GDN_ERR_UNSUPPORTED, "no decode kernel for d_k=%d d_v=%d", p.d_k, p.d_v);
+    if (p.B > 0 && (!q || !k || !v || !g || !beta || !state || !o))
+      return fail(GDN_ERR_NULL, "q, k, v, g, beta, state and o are required");
+    const void *ptrs[] = {q, k, v, g, beta, state, o};
+    const char *names[] = {"q", "k", "v", "g", "beta", "state", "o"};
+    for (int i = 0; i < 7; ++i)
+      if (ptrs[i] && !aligned16(ptrs[i])) return fail(GDN_ERR_ALIGN, "%s is not 16-byte aligned", names[i]);
+    const Tensors t = spans(p, q, k, v, g, beta, nullptr, nullptr, o, nullptr, nullptr, nullptr, 0);
+    const Span sst(state, (size_t)p.B * p.H_v * p.d_k * p.d_v * sizeof(float));
+    const Span ins[] = {t.q, t.k, t.v, t.g, t.beta};
+    const char *in_names[] = {"q", "k", "v", "g", "beta"};
+    for (int i = 0; i < 5; ++i) {
+      if (sst.overlaps(ins[i])) return fail(GDN_ERR_ALIAS, "state overlaps %s", in_names[i]);
+      if (t.o.overlaps(ins[i])) return fail(GDN_ERR_ALIAS, "o overlaps %s", in_names[i]);
+    }
+    if (t.o.overlaps(sst)) return fail(GDN_ERR_ALIAS, "o overlaps state");
+    gdn::StepArgs a{q, k, v, g, beta, state, o};
+    const hipError_t e = gdn::launch_recurrent_step(p, a, stream);
+    if (e != hipSuccess) return fail(GDN_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+    g_last_error.clear();
+    return GDN_OK;
+  } catch (...) {
+    return fail(GDN_ERR_HIP, "internal error");
+  }
+}
+
+}  // extern "C"

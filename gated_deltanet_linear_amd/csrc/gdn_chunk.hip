@@ -1,0 +1,721 @@
+// The chunked paths of libgdn: gdn_chunk_fwd and gdn_states_fwd.
+//
+// What is computed is the gated delta rule of the pages (Qwen3.5 text
+// encyclopedia page, note "The DeltaNet mixer"; value table of
+// model.layers[i].linear_attn) over chunks of C tokens.  Per value head, with
+// the in-chunk cumulative log decay G_r = g_0 + ... + g_r and S the state at
+// the chunk start, the token recurrence unrolls to (UT / WY form):
+//
+//   A[r,i] = beta_r e^{G_r - G_i} (k_r . k_i), i < r    strictly lower
+//   T      = (I + A)^{-1}                                unit lower
+//   U      = T diag(beta) (V - diag(e^G) K S)            the tokens' write vectors
+//   O      = diag(e^G) Q S + P U,  P[r,i] = e^{G_r-G_i} (q_r . k_i), i <= r
+//   S     <- e^{G_last} S + K^T diag(e^{G_last - G}) U
+//
+// Launch sequence on the caller's stream:
+//   plan   (1 workgroup)  sequence starts and chunk numbering from cu_seqlens
+//   prep   (chunk, qk head)  K K^T and Q K^T on MFMA, the fp32 triangular solve,
+//                           T diag(beta), P and the decay vectors -> workspace.
+//                           Both value heads of a query/key head share K K^T, Q K^T.
+//   carry  (sequence, value head, 32-column block of S)  walks the chunks of
+//                           one sequence in order with its S block in registers:
+//                           [Q;K] S, T diag(beta) X, P U and K^T U on MFMA.
+//                           The delta rule acts on each column of S on its own,
+//                           so column blocks are independent chains.
+//   stream (states path only)  S after every token from the chunk-start
+//                           state and the write vectors: S <- e^g S + k u^T,
+//                           one non-temporal 16-byte store per element group.
+//
+// Precision: S, all products' accumulators and the solve are fp32.  On the
+// bf16 path every operand that is a computed fp32 value (S, T diag(beta), X, P,
+// U) enters MFMA as a bf16 hi/lo pair (hi*hi + hi*lo + lo*hi); q, k, v are exact
+// bf16 inputs and enter once.  Decays are summed in fp64 and every factor
+// e^{G_r - G_i} is formed from a difference with r >= i, so it never overflows;
+// g is clamped to -1e4, which keeps -inf (a reset) finite and still gives
+// exp() == 0 for every factor that spans it.
+#include <type_traits>
+
+#include "gdn_device.hpp"
+#include "gdn_internal.hpp"
+#include "gdn.h"
+
+namespace gdn {
+
+constexpr float kGFloor = -1.0e4f;
+
+// ---------------------------------------------------------------------------
+// plan: sequence starts and the first global chunk of every sequence.
+// ---------------------------------------------------------------------------
+__global__ void plan_kernel(const int32_t *__restrict__ cu, int N, int T, int T_tot, int C,
+                            int max_chunks, int32_t *__restrict__ status,
+                            int32_t *__restrict__ seq_start, int32_t *__restrict__ chunk_first) {
+  if (threadIdx.x != 0) return;
+  int bad = 0, acc = 0, prev = 0;
+  for (int n = 0; n <= N; ++n) {
+    const int s = cu ? cu[n] : n * T;
+    if ((n == 0 && s != 0) || s < prev || s > T_tot) bad = 1;
+    seq_start[n] = s;
+    chunk_first[n] = acc;
+    if (n < N) {
+      const int e = cu ? cu[n + 1] : (n + 1) * T;
+      if (e >= s) acc += (e - s + C - 1) / C;
+    }
+    prev = s;
+  }
+  if (N >= 0 && (cu ? cu[N] : N * T) != T_tot) bad = 1;
+  if (acc > max_chunks) bad = 1;
+  *status = bad;
+}
+
+// Sequence n owning global chunk c: chunk_first[n] <= c < chunk_first[n+1].
+__device__ __forceinline__ int find_seq(const int32_t *chunk_first, int N, int c) {
+  int lo = 0, hi = N;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (chunk_first[mid] <= c) lo = mid;
+    else hi = mid;
+  }
+  return lo;
+}
+
+// Operand storage of a policy: bf16 path -> uint16_t (computed values as hi/lo
+// pairs), fp32 path -> float (single arrays, exact fp32 MFMA).
+template <typename TIn> struct Pol {
+  static constexpr bool BF = std::is_same<TIn, uint16_t>::value;
+  using CT = typename std::conditional<BF, uint16_t, float>::type;
+  static constexpr int PAD = BF ? 8 : 4;    // row padding in elements (16 bytes)
+  static constexpr int VEC = 16 / sizeof(TIn);
+};
+
+// acc += A[16 x kmax] * B[kmax x 16] for either policy.
+template <bool BF, int K, bool SA, bool SB, typename TA, typename TB>
+__device__ __forceinline__ void tile(f32x4 &acc, const TA *Ah, const TA *Al, int lda, const TB *Bh,
+                                     const TB *Bl, int ldb, int lane, int kmax = K) {
+  if constexpr (BF) {
+    tile_bf16<K, SA, SB>(acc, Ah, Al, lda, Bh, Bl, ldb, lane, kmax);
+  } else {
+    (void)Al;
+    (void)Bl;
+    tile_f32<K>(acc, Ah, lda, Bh, ldb, lane, kmax);
+  }
+}
+
+// Stores 4 fp32 values v[0..3] as consecutive elements at p (hi) and pl (lo).
+template <bool BF, typename CT>
+__device__ __forceinline__ void put4(CT *ph, CT *pl, const f32x4 &v) {
+  if constexpr (BF) {
+    uint16_t h[4], l[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) split_bf16(v[i], h[i], l[i]);
+    uint2 H, L;
+    H.x = (uint32_t)h[0] | ((uint32_t)h[1] << 16);
+    H.y = (uint32_t)h[2] | ((uint32_t)h[3] << 16);
+    L.x = (uint32_t)l[0] | ((uint32_t)l[1] << 16);
+    L.y = (uint32_t)l[2] | ((uint32_t)l[3] << 16);
+    *reinterpret_cast<uint2 *>(ph) = H;
+    *reinterpret_cast<uint2 *>(pl) = L;
+  } else {
+    (void)pl;
+    *reinterpret_cast<f32x4 *>(ph) = v;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// prep: per (chunk, query/key head), for each value head of the group.
+// ---------------------------------------------------------------------------
+template <typename TIn, int DK, int C> struct PrepSmem {
+  static constexpr int LDQ = DK + Pol<TIn>::PAD;
+  static constexpr int LDC = C + 4;
+  alignas(16) TIn q[C * LDQ];
+  alignas(16) TIn k[C * LDQ];
+  alignas(16) float G[C * LDC];   // K K^T (lower tiles)
+  alignas(16) float QK[C * LDC];  // Q K^T (lower tiles)
+  alignas(16) float A[C * LDC];
+  alignas(16) float Tm[C * LDC];
+  alignas(16) float Y[4][16 * 16];
+  alignas(16) double gam[C];
+  float beta[C];
+  float rq[C], rk[C];
+};
+
+template <typename TIn, int DK, int C>
+__global__ __launch_bounds__(256) void prep_kernel(
+    const TIn *__restrict__ q, const TIn *__restrict__ k, const float *__restrict__ g,
+    const float *__restrict__ beta, const int32_t *__restrict__ status,
+    const int32_t *__restrict__ seq_start, const int32_t *__restrict__ chunk_first,
+    float *__restrict__ tb, float *__restrict__ pm, float *__restrict__ eg, float *__restrict__ eb,
+    int N, int H_qk, int H_v, float scale, int l2norm) {
+  using P = Pol<TIn>;
+  using S = PrepSmem<TIn, DK, C>;
+  constexpr int LDQ = S::LDQ, LDC = S::LDC, VEC = P::VEC, VPR = DK / VEC, NB = C / 16;
+  static_assert(C % 16 == 0 && C <= 64 && DK % VEC == 0, "prep tiling");
+  __shared__ S sm;
+
+  if (*status) return;
+  const int c = blockIdx.x;
+  if (c >= chunk_first[N]) return;
+  const int n = find_seq(chunk_first, N, c);
+  const int t0 = seq_start[n] + (c - chunk_first[n]) * C;
+  const int len = min(C, seq_start[n + 1] - t0);
+  const int j = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lr = lane & 15, lg = lane >> 4;
+
+  // q, k rows of this chunk (zero beyond len).
+  for (int x = tid; x < C * VPR; x += 256) {
+    const int r = x / VPR, cv = x % VPR;
+    uint4 qv = {0u, 0u, 0u, 0u}, kv = {0u, 0u, 0u, 0u};
+    if (r < len) {
+      const int64_t off = ((int64_t)(t0 + r) * H_qk + j) * DK + cv * VEC;
+      qv = *reinterpret_cast<const uint4 *>(q + off);
+      kv = *reinterpret_cast<const uint4 *>(k + off);
+    }
+    *reinterpret_cast<uint4 *>(sm.q + r * LDQ + cv * VEC) = qv;
+    *reinterpret_cast<uint4 *>(sm.k + r * LDQ + cv * VEC) = kv;
+  }
+  __syncthreads();
+  if (tid < C) {
+    float rq = 1.f, rk = 1.f;
+    if (l2norm) {
+      float sq = 0.f, sk = 0.f;
+      for (int i = 0; i < DK; ++i) {
+        const float a = Elem<TIn>::get(sm.q, tid * LDQ + i), b = Elem<TIn>::get(sm.k, tid * LDQ + i);
+        sq += a * a;
+        sk += b * b;
+      }
+      rq = 1.0f / sqrtf(sq + 1e-6f);
+      rk = 1.0f / sqrtf(sk + 1e-6f);
+    }
+    sm.rq[tid] = rq * scale;
+    sm.rk[tid] = rk;
+  }
+
+  // K K^T and Q K^T: the lower 16x16 tiles (diagonal included) on MFMA.
+  constexpr int NTRI = NB * (NB + 1) / 2;
+  for (int t = wave; t < 2 * NTRI; t += 4) {
+    const bool isq = t >= NTRI;
+    const int tt = isq ? t - NTRI : t;
+    int mi = 0;
+    while ((mi + 1) * (mi + 2) / 2 <= tt) ++mi;
+    const int ni = tt - mi * (mi + 1) / 2;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    const TIn *Ab = (isq ? sm.q : sm.k) + mi * 16 * LDQ;
+    const TIn *Bb = sm.k + ni * 16 * LDQ;
+    tile<P::BF, DK, false, false>(acc, Ab, Ab, LDQ, Bb, Bb, LDQ, lane);
+    float *D = isq ? sm.QK : sm.G;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) D[(mi * 16 + 4 * lg + i) * LDC + ni * 16 + lr] = acc[i];
+  }
+  __syncthreads();
+
+  const int R = H_v / H_qk;
+  for (int rr = 0; rr < R; ++rr) {
+    const int h = j * R + rr;
+    const int64_t slot = (int64_t)c * H_v + h;
+    if (wave == 0) {
+      double gv = 0.0;
+      float bv = 0.f;
+      if (lane < len) {
+        gv = (double)fmaxf(g[(int64_t)(t0 + lane) * H_v + h], kGFloor);
+        bv = beta[(int64_t)(t0 + lane) * H_v + h];
+      }
+      const double gam = wave_inclusive_scan(gv, lane);
+      if (lane < C) {
+        sm.gam[lane] = gam;
+        sm.beta[lane] = bv;
+      }
+    }
+    __syncthreads();
+    const double glast = sm.gam[C - 1];
+    for (int x = tid; x < C * C; x += 256) {
+      const int r = x / C, i = x - r * C;
+      float a = 0.f, pv = 0.f;
+      if (i <= r) {
+        const float dec = expf((float)(sm.gam[r] - sm.gam[i]));
+        pv = sm.rq[r] * sm.rk[i] * dec * sm.QK[r * LDC + i];
+        if (i < r) a = sm.beta[r] * dec * sm.rk[r] * sm.rk[i] * sm.G[r * LDC + i];
+      }
+      sm.A[r * LDC + i] = a;
+      pm[slot * C * C + x] = pv;
+    }
+    if (tid < C) {
+      eg[slot * C + tid] = expf((float)sm.gam[tid]);
+      eb[slot * C + tid] = expf((float)(glast - sm.gam[tid]));
+    }
+    __syncthreads();
+
+    // T = (I + A)^{-1}.  Diagonal 16x16 blocks by forward substitution: lane
+    // 16*b + c owns column c of block b.
+    if (wave == 0 && lane < C) {
+      const int bb = lane >> 4, cc = lane & 15;
+      const float *Ab = sm.A + (bb * 16) * LDC + bb * 16;
+      float col[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float s = (r == cc) ? 1.f : 0.f;
+#pragma unroll
+        for (int m = 0; m < r; ++m) s -= Ab[r * LDC + m] * col[m];
+        col[r] = s;
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sm.Tm[(bb * 16 + r) * LDC + bb * 16 + cc] = col[r];
+    }
+    __syncthreads();
+    // Off-diagonal blocks, nearest the diagonal first:
+    //   T_ij = -T_ii * sum_{m=j}^{i-1} A_im T_mj    (wave w: block row i = d + w)
+    for (int d = 1; d < NB; ++d) {
+      const int ib = d + wave, jb = ib - d;
+      if (ib < NB) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * lg + e;
+          float s = 0.f;
+          for (int m = jb; m < ib; ++m)
+#pragma unroll
+            for (int x = 0; x < 16; ++x)
+              s += sm.A[(ib * 16 + r) * LDC + m * 16 + x] * sm.Tm[(m * 16 + x) * LDC + jb * 16 + lr];
+          sm.Y[wave][r * 16 + lr] = s;
+        }
+      }
+      __syncthreads();
+      if (ib < NB) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * lg + e;
+          float s = 0.f;
+#pragma unroll
+          for (int x = 0; x < 16; ++x) s += sm.Tm[(ib * 16 + r) * LDC + ib * 16 + x] * sm.Y[wave][x * 16 + lr];
+          sm.Tm[(ib * 16 + r) * LDC + jb * 16 + lr] = -s;
+        }
+      }
+      __syncthreads();
+    }
+    for (int x = tid; x < C * C; x += 256) {
+      const int r = x / C, i = x - r * C;
+      tb[slot * C * C + x] = (i <= r) ? sm.Tm[r * LDC + i] * sm.beta[i] : 0.f;
+    }
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------
+// carry: one (sequence, value head, DVB-column block of S) walks its chunks.
+// ---------------------------------------------------------------------------
+template <typename TIn, int DK, int C, int DVB> struct CarrySmem {
+  using CT = typename Pol<TIn>::CT;
+  static constexpr bool BF = Pol<TIn>::BF;
+  static constexpr int PAD = Pol<TIn>::PAD;
+  static constexpr int LDQ = DK + PAD;   // Q, K      [C][LDQ]
+  static constexpr int LDKT = C + PAD;   // K^T       [DK][LDKT]
+  static constexpr int LDST = DK + PAD;  // S^T       [DVB][LDST]
+  static constexpr int LDX = C + PAD;    // Tb, P     [C][LDX];  X^T, U^T, U2^T [DVB][LDX]
+  static constexpr int LO = BF ? 1 : 0;  // lo halves exist only on the bf16 path
+  alignas(16) TIn q[C * LDQ];
+  alignas(16) TIn k[C * LDQ];
+  alignas(16) TIn kt[DK * LDKT];
+  alignas(16) TIn v[C * DVB];
+  alignas(16) CT tbh[C * LDX];
+  alignas(16) CT tbl[LO ? C * LDX : 4];
+  alignas(16) CT ph[C * LDX];
+  alignas(16) CT pl[LO ? C * LDX : 4];
+  alignas(16) CT sth[DVB * LDST];
+  alignas(16) CT stl[LO ? DVB * LDST : 4];
+  alignas(16) CT xth[DVB * LDX];
+  alignas(16) CT xtl[LO ? DVB * LDX : 4];
+  alignas(16) CT uth[DVB * LDX];
+  alignas(16) CT utl[LO ? DVB * LDX : 4];
+  alignas(16) CT u2h[DVB * LDX];
+  alignas(16) CT u2l[LO ? DVB * LDX : 4];
+  alignas(16) float eg[C], eb[C], rq[C], rk[C];
+};
+
+template <typename TIn, int DK, int C, int DVB, bool STATES, bool OBF16>
+__global__ __launch_bounds__(256) void carry_kernel(
+    const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__restrict__ v,
+    const float *__restrict__ s0, const int32_t *__restrict__ status,
+    const int32_t *__restrict__ seq_start, const int32_t *__restrict__ chunk_first,
+    const float *__restrict__ tbw, const float *__restrict__ pmw, const float *__restrict__ egw,
+    const float *__restrict__ ebw, void *__restrict__ o, float *__restrict__ fin,
+    float *__restrict__ uw, float *__restrict__ scw, int N, int H_qk, int H_v, int d_v, float scale,
+    int l2norm, int units, int grid) {
+  using P = Pol<TIn>;
+  using SM = CarrySmem<TIn, DK, C, DVB>;
+  using CT = typename SM::CT;
+  constexpr bool BF = P::BF;
+  constexpr int LDQ = SM::LDQ, LDKT = SM::LDKT, LDST = SM::LDST, LDX = SM::LDX;
+  constexpr int VEC = P::VEC, VPR = DK / VEC, VPV = DVB / VEC;
+  constexpr int NMT = DK / 16, NNT = DVB / 16, NST = NMT * NNT, SPW = (NST + 3) / 4;
+  constexpr int NRT = C / 16, MTW = (NRT + 3) / 4;
+  static_assert(C % 16 == 0 && DK % 16 == 0 && DVB % 16 == 0 && DVB % VEC == 0, "carry tiling");
+  __shared__ SM sm;
+
+  if (*status) return;
+  const int u = xcd_remap(blockIdx.x, grid);
+  if (u >= units) return;
+  const int NJB = d_v / DVB;
+  const int jb = u % NJB, h = (u / NJB) % H_v, n = u / (NJB * H_v);
+  const int j = h / (H_v / H_qk);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lr = lane & 15, lg = lane >> 4;
+  const int col0 = jb * DVB;
+
+  // This wave's tiles of the S block: tile id wave + 4 s -> (row tile, col tile).
+  f32x4 S[SPW];
+#pragma unroll
+  for (int s = 0; s < SPW; ++s) {
+    S[s] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int t = wave + 4 * s;
+    if (t < NST && s0) {
+      const int mi = t / NNT, ni = t % NNT;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        S[s][i] = s0[((int64_t)(n * H_v + h) * DK + mi * 16 + 4 * lg + i) * d_v + col0 + ni * 16 + lr];
+    }
+  }
+
+  const int c_begin = chunk_first[n], c_end = chunk_first[n + 1];
+  const int s_begin = seq_start[n], s_end = seq_start[n + 1];
+  for (int c = c_begin; c < c_end; ++c) {
+    const int t0 = s_begin + (c - c_begin) * C;
+    const int len = min(C, s_end - t0);
+    const int64_t slot = (int64_t)c * H_v + h;
+    __syncthreads();  // the previous chunk is done with every LDS buffer
+
+    // q, k rows and the transposed k; zero beyond len.
+    for (int x = tid; x < C * VPR; x += 256) {
+      const int r = x / VPR, cv = x % VPR;
+      uint4 qv = {0u, 0u, 0u, 0u}, kv = {0u, 0u, 0u, 0u};
+      if (r < len) {
+        const int64_t off = ((int64_t)(t0 + r) * H_qk + j) * DK + cv * VEC;
+        qv = *reinterpret_cast<const uint4 *>(q + off);
+        kv = *reinterpret_cast<const uint4 *>(k + off);
+      }
+      *reinterpret_cast<uint4 *>(sm.q + r * LDQ + cv * VEC) = qv;
+      *reinterpret_cast<uint4 *>(sm.k + r * LDQ + cv * VEC) = kv;
+      const TIn *ke = reinterpret_cast<const TIn *>(&kv);
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) sm.kt[(cv * VEC + e) * LDKT + r] = ke[e];
+    }
+    // v block [C][DVB]
+    for (int x = tid; x < C * VPV; x += 256) {
+      const int r = x / VPV, cv = x % VPV;
+      uint4 vv = {0u, 0u, 0u, 0u};
+      if (r < len) vv = *reinterpret_cast<const uint4 *>(v + ((int64_t)(t0 + r) * H_v + h) * d_v + col0 + cv * VEC);
+      *reinterpret_cast<uint4 *>(sm.v + r * DVB + cv * VEC) = vv;
+    }
+    // T diag(beta) and P from the prep phase, split for MFMA.
+    for (int x = tid; x < C * C / 4; x += 256) {
+      const int r = (4 * x) / C, i = (4 * x) % C;
+      const f32x4 a = *reinterpret_cast<const f32x4 *>(tbw + slot * C * C + 4 * x);
+      const f32x4 b = *reinterpret_cast<const f32x4 *>(pmw + slot * C * C + 4 * x);
+      put4<BF>(sm.tbh + r * LDX + i, sm.tbl + (BF ? r * LDX + i : 0), a);
+      put4<BF>(sm.ph + r * LDX + i, sm.pl + (BF ? r * LDX + i : 0), b);
+    }
+    if (tid < C) {
+      sm.eg[tid] = egw[slot * C + tid];
+      sm.eb[tid] = ebw[slot * C + tid];
+      if (!l2norm) {
+        sm.rq[tid] = scale;
+        sm.rk[tid] = 1.f;
+      }
+    }
+    // S -> S^T (split) for [Q;K] S; the states path also keeps the chunk-start state.
+#pragma unroll
+    for (int s = 0; s < SPW; ++s) {
+      const int t = wave + 4 * s;
+      if (t < NST) {
+        const int mi = t / NNT, ni = t % NNT;
+        const int cn = ni * 16 + lr, rk0 = mi * 16 + 4 * lg;
+        put4<BF>(sm.sth + cn * LDST + rk0, sm.stl + (BF ? cn * LDST + rk0 : 0), S[s]);
+        if constexpr (STATES) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) scw[(slot * DK + rk0 + i) * d_v + col0 + cn] = S[s][i];
+        }
+      }
+    }
+    __syncthreads();
+    if (l2norm) {
+      if (tid < 2 * C) {
+        const int r = tid % C;
+        const TIn *row = (tid < C ? sm.q : sm.k) + r * LDQ;
+        float ss = 0.f;
+        for (int i = 0; i < DK; ++i) {
+          const float a = Elem<TIn>::get(row, i);
+          ss += a * a;
+        }
+        const float rn = 1.0f / sqrtf(ss + 1e-6f);
+        if (tid < C) sm.rq[r] = rn * scale;
+        else sm.rk[r] = rn;
+      }
+      __syncthreads();
+    }
+
+    // [Q;K] S for this wave's chunk row tiles; X = V - e^G * (K S) -> X^T.
+    f32x4 qsc[MTW][NNT];
+#pragma unroll
+    for (int w = 0; w < MTW; ++w) {
+      const int mt = wave + 4 * w;
+      if (mt < NRT) {
+#pragma unroll
+        for (int ni = 0; ni < NNT; ++ni) {
+          f32x4 qa = {0.f, 0.f, 0.f, 0.f}, ka = {0.f, 0.f, 0.f, 0.f};
+          const CT *bh = sm.sth + ni * 16 * LDST;
+          const CT *bl = sm.stl + (BF ? ni * 16 * LDST : 0);
+          tile<BF, DK, false, true>(qa, sm.q + mt * 16 * LDQ, sm.q, LDQ, bh, bl, LDST, lane);
+          tile<BF, DK, false, true>(ka, sm.k + mt * 16 * LDQ, sm.k, LDQ, bh, bl, LDST, lane);
+          f32x4 xv;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int r = mt * 16 + 4 * lg + i;
+            const float vr = Elem<TIn>::get(sm.v, r * DVB + ni * 16 + lr);
+            xv[i] = vr - sm.eg[r] * sm.rk[r] * ka[i];
+            qa[i] *= sm.eg[r] * sm.rq[r];
+          }
+          qsc[w][ni] = qa;
+          const int cn = ni * 16 + lr, r0 = mt * 16 + 4 * lg;
+          put4<BF>(sm.xth + cn * LDX + r0, sm.xtl + (BF ? cn * LDX + r0 : 0), xv);
+        }
+      }
+    }
+    __syncthreads();
+
+    // U = T diag(beta) X  (lower triangular: row tile mt needs columns < 16 (mt+1)).
+#pragma unroll
+    for (int w = 0; w < MTW; ++w) {
+      const int mt = wave + 4 * w;
+      if (mt < NRT) {
+#pragma unroll
+        for (int ni = 0; ni < NNT; ++ni) {
+          f32x4 ua = {0.f, 0.f, 0.f, 0.f};
+          tile<BF, C, true, true>(ua, sm.tbh + mt * 16 * LDX, sm.tbl + (BF ? mt * 16 * LDX : 0), LDX,
+                                  sm.xth + ni * 16 * LDX, sm.xtl + (BF ? ni * 16 * LDX : 0), LDX, lane,
+                                  16 * (mt + 1));
+          f32x4 u2;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int r = mt * 16 + 4 * lg + i;
+            u2[i] = sm.eb[r] * sm.rk[r] * ua[i];
+            if constexpr (STATES) {
+              if (r < len) uw[((int64_t)(t0 + r) * H_v + h) * d_v + col0 + ni * 16 + lr] = ua[i];
+            }
+          }
+          const int cn = ni * 16 + lr, r0 = mt * 16 + 4 * lg;
+          put4<BF>(sm.uth + cn * LDX + r0, sm.utl + (BF ? cn * LDX + r0 : 0), ua);
+          put4<BF>(sm.u2h + cn * LDX + r0, sm.u2l + (BF ? cn * LDX + r0 : 0), u2);
+        }
+      }
+    }
+    __syncthreads();
+
+    // O = e^G Q S + P U -> o (rows < len).
+#pragma unroll
+    for (int w = 0; w < MTW; ++w) {
+      const int mt = wave + 4 * w;
+      if (mt < NRT) {
+#pragma unroll
+        for (int ni = 0; ni < NNT; ++ni) {
+          f32x4 oa = qsc[w][ni];
+          tile<BF, C, true, true>(oa, sm.ph + mt * 16 * LDX, sm.pl + (BF ? mt * 16 * LDX : 0), LDX,
+                                  sm.uth + ni * 16 * LDX, sm.utl + (BF ? ni * 16 * LDX : 0), LDX, lane,
+                                  16 * (mt + 1));
+          if (o) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int r = mt * 16 + 4 * lg + i;
+              if (r < len) {
+                const int64_t oi = ((int64_t)(t0 + r) * H_v + h) * d_v + col0 + ni * 16 + lr;
+                if constexpr (OBF16) reinterpret_cast<uint16_t *>(o)[oi] = f2bf(oa[i]);
+                else reinterpret_cast<float *>(o)[oi] = oa[i];
+              }
+            }
+          }
+        }
+      }
+    }
+    // S <- e^{G_last} S + K^T diag(e^{G_last - G}) U.
+    const float elast = sm.eg[C - 1];
+#pragma unroll
+    for (int s = 0; s < SPW; ++s) {
+      const int t = wave + 4 * s;
+      if (t < NST) {
+        const int mi = t / NNT, ni = t % NNT;
+        S[s] *= elast;
+        tile<BF, C, false, true>(S[s], sm.kt + mi * 16 * LDKT, sm.kt, LDKT, sm.u2h + ni * 16 * LDX,
+                                 sm.u2l + (BF ? ni * 16 * LDX : 0), LDX, lane);
+      }
+    }
+  }
+
+  if (fin) {
+#pragma unroll
+    for (int s = 0; s < SPW; ++s) {
+      const int t = wave + 4 * s;
+      if (t < NST) {
+        const int mi = t / NNT, ni = t % NNT;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          fin[((int64_t)(n * H_v + h) * DK + mi * 16 + 4 * lg + i) * d_v + col0 + ni * 16 + lr] = S[s][i];
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// stream: the state after every token, S <- e^{g_t} S + k_t u_t^T, from the
+// chunk-start state and the write vectors of the carry phase.  Workgroup =
+// (chunk, value head, block of RB rows of S); thread = 4 columns of one row.
+// ---------------------------------------------------------------------------
+template <typename TIn, int C>
+__global__ __launch_bounds__(256) void stream_kernel(
+    const TIn *__restrict__ k, const float *__restrict__ g, const float *__restrict__ uw,
+    const float *__restrict__ scw, const int32_t *__restrict__ status,
+    const int32_t *__restrict__ seq_start, const int32_t *__restrict__ chunk_first,
+    float *__restrict__ states, int N, int H_qk, int H_v, int d_k, int d_v, int l2norm) {
+  extern __shared__ float ssm[];  // u [C][d_v], kk [C][RB], alpha [C]
+  if (*status) return;
+  const int c = blockIdx.x;
+  if (c >= chunk_first[N]) return;
+  const int n = find_seq(chunk_first, N, c);
+  const int t0 = seq_start[n] + (c - chunk_first[n]) * C;
+  const int len = min(C, seq_start[n + 1] - t0);
+  const int h = blockIdx.y, j = h / (H_v / H_qk);
+  const int CGn = d_v / 4, RB = 256 / CGn;
+  const int row0 = blockIdx.z * RB;
+  const int tid = threadIdx.x, cg = tid % CGn, rl = tid / CGn;
+  float *us = ssm, *kk = ssm + C * d_v, *al = kk + C * RB;
+  const int64_t slot = (int64_t)c * H_v + h;
+
+  for (int x = tid; x < len * CGn; x += 256) {
+    const int r = x / CGn, cc = x % CGn;
+    *reinterpret_cast<f32x4 *>(us + r * d_v + 4 * cc) =
+        *reinterpret_cast<const f32x4 *>(uw + ((int64_t)(t0 + r) * H_v + h) * d_v + 4 * cc);
+  }
+  if (tid < len) {
+    const int r = tid;
+    const TIn *kr = k + ((int64_t)(t0 + r) * H_qk + j) * d_k;
+    float rk = 1.f;
+    if (l2norm) {
+      float ss = 0.f;
+      for (int i = 0; i < d_k; ++i) {
+        const float a = Elem<TIn>::get(kr, i);
+        ss += a * a;
+      }
+      rk = 1.0f / sqrtf(ss + 1e-6f);
+    }
+    for (int i = 0; i < RB; ++i) kk[r * RB + i] = (row0 + i < d_k) ? Elem<TIn>::get(kr, row0 + i) * rk : 0.f;
+    al[r] = expf(g[(int64_t)(t0 + r) * H_v + h]);
+  }
+  __syncthreads();
+  const int row = row0 + rl;
+  if (rl >= RB || row >= d_k) return;  // tail threads when 256 % (d_v / 4) != 0
+  f32x4 Sv = *reinterpret_cast<const f32x4 *>(scw + (slot * d_k + row) * d_v + 4 * cg);
+  const int64_t sstride = (int64_t)H_v * d_k * d_v;
+  f32x4 *dst = reinterpret_cast<f32x4 *>(states + ((int64_t)t0 * H_v + h) * d_k * d_v + (int64_t)row * d_v + 4 * cg);
+  for (int r = 0; r < len; ++r) {
+    const f32x4 uv = *reinterpret_cast<const f32x4 *>(us + r * d_v + 4 * cg);
+    Sv = al[r] * Sv + kk[r * RB + rl] * uv;
+    __builtin_nontemporal_store(Sv, dst);
+    dst += sstride / 4;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// host launchers
+// ---------------------------------------------------------------------------
+template <typename TIn, int DK, int C, int DVB, bool STATES, bool OBF16>
+static hipError_t run_t(const Problem &p, const ChunkArgs &a, hipStream_t st) {
+  const Workspace &w = a.ws;
+  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(64), 0, st, a.cu, p.N, p.T, p.T_tot, p.C, p.max_chunks,
+                     w.status, w.seq_start, w.chunk_first);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const TIn *q = static_cast<const TIn *>(a.q), *k = static_cast<const TIn *>(a.k),
+            *v = static_cast<const TIn *>(a.v);
+  if (p.max_chunks > 0 && p.H_qk > 0) {
+    hipLaunchKernelGGL((prep_kernel<TIn, DK, C>), dim3(p.max_chunks, p.H_qk), dim3(256), 0, st, q, k, a.g,
+                       a.beta, w.status, w.seq_start, w.chunk_first, w.tb, w.pm, w.eg, w.eb, p.N, p.H_qk,
+                       p.H_v, p.scale, p.l2norm ? 1 : 0);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  const int units = p.N * p.H_v * (p.d_v / DVB);
+  if (units > 0) {
+    const int grid = (units + 7) / 8 * 8;
+    hipLaunchKernelGGL((carry_kernel<TIn, DK, C, DVB, STATES, OBF16>), dim3(grid), dim3(256), 0, st, q, k, v,
+                       a.s0, w.status, w.seq_start, w.chunk_first, w.tb, w.pm, w.eg, w.eb, a.o,
+                       a.final_state, w.u, w.sc, p.N, p.H_qk, p.H_v, p.d_v, p.scale, p.l2norm ? 1 : 0, units,
+                       grid);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  if constexpr (STATES) {
+    const int CGn = p.d_v / 4, RB = 256 / CGn;
+    const int zb = ceil_div(p.d_k, RB);
+    if (p.max_chunks > 0 && p.H_v > 0 && zb > 0) {
+      const size_t shm = sizeof(float) * ((size_t)C * p.d_v + (size_t)C * RB + C);
+      hipLaunchKernelGGL((stream_kernel<TIn, C>), dim3(p.max_chunks, p.H_v, zb), dim3(256), shm, st, k, a.g,
+                         w.u, w.sc, w.status, w.seq_start, w.chunk_first, a.states, p.N, p.H_qk, p.H_v,
+                         p.d_k, p.d_v, p.l2norm ? 1 : 0);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+  }
+  return hipSuccess;
+}
+
+template <typename TIn, int DK, int C, int DVB>
+static hipError_t run_cfg(const Problem &p, const ChunkArgs &a, bool states, hipStream_t st) {
+  const bool ob = p.o_dtype == GDN_BF16;
+  if (states) return ob ? run_t<TIn, DK, C, DVB, true, true>(p, a, st) : run_t<TIn, DK, C, DVB, true, false>(p, a, st);
+  return ob ? run_t<TIn, DK, C, DVB, false, true>(p, a, st) : run_t<TIn, DK, C, DVB, false, false>(p, a, st);
+}
+
+bool chunk_path_supported(const Problem &p) {
+  // d_v <= 128 keeps the states stream's LDS staging (C x d_v fp32) within 64 KiB.
+  if (p.dtype == GDN_BF16) return p.d_k == 128 && p.C == 64 && p.d_v % 32 == 0 && p.d_v <= 128;
+  return p.d_k == 16 && p.C == 16 && p.d_v % 16 == 0 && p.d_v <= 128;
+}
+
+hipError_t launch_chunk_path(const Problem &p, const ChunkArgs &a, bool states, hipStream_t st) {
+  if (p.dtype == GDN_BF16 && p.d_k == 128 && p.C == 64) return run_cfg<uint16_t, 128, 64, 32>(p, a, states, st);
+  if (p.dtype == GDN_F32 && p.d_k == 16 && p.C == 16) return run_cfg<float, 16, 16, 16>(p, a, states, st);
+  return hipErrorInvalidValue;
+}
+
+Workspace workspace_layout(const Problem &p, bool states, void *base) {
+  Workspace w;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = align_up(off + bytes, 256);
+    return at;
+  };
+  const size_t st = take(sizeof(int32_t));
+  const size_t ss = take(sizeof(int32_t) * ((size_t)p.N + 1));
+  const size_t cf = take(sizeof(int32_t) * ((size_t)p.N + 1));
+  const size_t cc = (size_t)p.max_chunks * p.H_v;
+  const size_t tb = take(sizeof(float) * cc * p.C * p.C);
+  const size_t pm = take(sizeof(float) * cc * p.C * p.C);
+  const size_t eg = take(sizeof(float) * cc * p.C);
+  const size_t eb = take(sizeof(float) * cc * p.C);
+  size_t uo = 0, so = 0;
+  if (states) {
+    uo = take(sizeof(float) * (size_t)p.T_tot * p.H_v * p.d_v);
+    so = take(sizeof(float) * cc * p.d_k * p.d_v);
+  }
+  w.bytes = off;
+  if (base) {
+    char *b = static_cast<char *>(base);
+    w.status = reinterpret_cast<int32_t *>(b + st);
+    w.seq_start = reinterpret_cast<int32_t *>(b + ss);
+    w.chunk_first = reinterpret_cast<int32_t *>(b + cf);
+    w.tb = reinterpret_cast<float *>(b + tb);
+    w.pm = reinterpret_cast<float *>(b + pm);
+    w.eg = reinterpret_cast<float *>(b + eg);
+    w.eb = reinterpret_cast<float *>(b + eb);
+    if (states) {
+      w.u = reinterpret_cast<float *>(b + uo);
+      w.sc = reinterpret_cast<float *>(b + so);
+    }
+  }
+  return w;
+}
+
+}  // namespace gdn

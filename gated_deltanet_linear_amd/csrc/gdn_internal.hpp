@@ -1,0 +1,73 @@
+// Host-side interface between the C ABI layer (gdn_api.cpp) and the kernel
+// translation units: the workspace layout and the launchers.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace gdn {
+
+// Problem description after validation (all sizes non-negative, H_v % H_qk == 0).
+struct Problem {
+  int B, T, H_qk, H_v, d_k, d_v, C;
+  int N;              // sequences: num_seqs with cu_seqlens, else B
+  int T_tot;          // tokens on the packed axis: B * T
+  int max_chunks;     // upper bound on the chunk count (grid size of the chunk-parallel phase)
+  float scale;
+  int dtype, o_dtype; // GDN_F32 / GDN_BF16
+  bool l2norm;
+  bool packed;        // cu_seqlens given
+};
+
+inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Workspace of the chunked paths, carved out of the caller's buffer:
+//   status      int32            plan result: 0 ok, nonzero = bad cu_seqlens
+//   seq_start   int32 [N+1]      token offset of each sequence (cu_seqlens or n*T)
+//   chunk_first int32 [N+1]      global index of each sequence's first chunk
+//   tb          f32 [max_chunks, H_v, C, C]   T diag(beta), T = (I + A)^-1
+//   pm          f32 [max_chunks, H_v, C, C]   scale * (decay mask o Q K^T)
+//   eg          f32 [max_chunks, H_v, C]      exp(G_r)          (G: in-chunk cumsum of g)
+//   eb          f32 [max_chunks, H_v, C]      exp(G_last - G_r)
+//   (states path only)
+//   u           f32 [T_tot, H_v, d_v]        per-token write vectors
+//   sc          f32 [max_chunks, H_v, d_k, d_v]  state at each chunk start
+struct Workspace {
+  int32_t *status = nullptr;
+  int32_t *seq_start = nullptr;
+  int32_t *chunk_first = nullptr;
+  float *tb = nullptr, *pm = nullptr, *eg = nullptr, *eb = nullptr;
+  float *u = nullptr, *sc = nullptr;
+  size_t bytes = 0;
+};
+
+// Computes the layout; with base == nullptr only `bytes` is meaningful.
+Workspace workspace_layout(const Problem &p, bool states, void *base);
+
+// Launchers: return hipSuccess or the launch error.  Pointers are device pointers.
+struct ChunkArgs {
+  const void *q, *k, *v;
+  const float *g, *beta, *s0;
+  const int32_t *cu;   // may be null (dense rows)
+  void *o;             // may be null (states path)
+  float *final_state;  // may be null
+  float *states;       // states path only
+  Workspace ws;
+};
+hipError_t launch_chunk_path(const Problem &p, const ChunkArgs &a, bool states, hipStream_t stream);
+
+// True when a chunked-path kernel is built for this problem.
+bool chunk_path_supported(const Problem &p);
+
+struct StepArgs {
+  const void *q, *k, *v;
+  const float *g, *beta;
+  float *state;
+  void *o;
+};
+hipError_t launch_recurrent_step(const Problem &p, const StepArgs &a, hipStream_t stream);
+bool step_supported(const Problem &p);
+
+}  // namespace gdn

@@ -1,0 +1,170 @@
+/*
+ * libgdn: the gated delta rule on AMD Instinct MI355X (gfx950).
+ *
+ * The gated delta rule is the recurrent mixer of the Qwen3.5 / Qwen3-Next hybrid
+ * blocks (Qwen3.5 text encyclopedia page, note "The DeltaNet mixer"; Qwen3-Next
+ * encyclopedia page, note "The DeltaNet mixer fuses its projections per key head").
+ * Per value head it keeps a float32 state S of shape [d_k, d_v] and, per token t,
+ *
+ *     S <- exp(g_t) S                        g_t: the token's log decay ("decays")
+ *     S <- S + k_t (beta_t (v_t - S^T k_t))^T  beta_t: the write strength ("betas")
+ *     o_t = S^T q_t                          read after the write
+ *
+ * where q_t and k_t are optionally L2-normalised in the kernel (GDN_QK_L2NORM:
+ * x / sqrt(sum x^2 + 1e-6)) and q_t is multiplied by `scale` (the pages use
+ * 1/sqrt(128)).  Query/key heads are shared by groups of value heads the way
+ * repeat_interleave shares them: value head h reads query/key head
+ * h / (H_v / H_qk).  The call shapes mirror the pages' kernel call: q, k, v
+ * (elements 0-2), g, beta, initial_state in; the output and the state leaving
+ * the layer out, or the state after every token (Qwen3.5 text encyclopedia
+ * page, value table of model.layers[i].linear_attn).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every tensor pointer is DEVICE memory owned by the caller.  The library
+ *    never allocates, frees or synchronises: it validates on the host, enqueues
+ *    its kernels on `stream`, and returns.
+ *  - Tensors are dense and row-major in exactly the layouts stated below.
+ *  - Validation runs on the host before any launch: on failure the call
+ *    returns a status, records a message for gdn_last_error(), and writes
+ *    nothing.  A failed launch returns GDN_ERR_HIP.  Device faults surface at
+ *    the caller's next synchronisation.  No C++ exception crosses this ABI.
+ *  - Calls are reentrant; gdn_last_error() is per host thread.
+ *  - All pointers must be 16-byte aligned.
+ */
+#ifndef GDN_H
+#define GDN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  GDN_OK = 0,
+  GDN_ERR_NULL = 1,        /* a required pointer is NULL                        */
+  GDN_ERR_SHAPE = 2,       /* a size is negative, zero where it may not be, or
+                              H_v is not a multiple of H_qk                      */
+  GDN_ERR_DTYPE = 3,       /* unknown dtype / o_dtype value                     */
+  GDN_ERR_UNSUPPORTED = 4, /* valid, but no kernel is built for this (d_k, d_v,
+                              chunk, dtype) combination                          */
+  GDN_ERR_ALIAS = 5,       /* an output overlaps an input it may not overlap    */
+  GDN_ERR_ALIGN = 6,       /* a pointer is not 16-byte aligned                  */
+  GDN_ERR_WORKSPACE = 7,   /* workspace missing or smaller than the query says  */
+  GDN_ERR_HIP = 8          /* a HIP launch failed                               */
+} gdn_status;
+
+/* Element types.  GDN_F32 = float32, GDN_BF16 = bfloat16. */
+enum { GDN_F32 = 0, GDN_BF16 = 1 };
+
+/* flags */
+enum { GDN_QK_L2NORM = 1u << 0 };
+
+typedef struct {
+  int32_t B;       /* rows; with cu_seqlens B must be 1                          */
+  int32_t T;       /* tokens per row; with cu_seqlens, the total token count     */
+  int32_t H_qk;    /* query/key heads                                             */
+  int32_t H_v;     /* value heads, a multiple of H_qk                             */
+  int32_t d_k;     /* key width                                                   */
+  int32_t d_v;     /* value width                                                 */
+  int32_t chunk;   /* tokens per chunk of the chunked path (ignored by the step)  */
+  float scale;     /* multiplies q (after the optional L2 norm)                   */
+  int32_t dtype;   /* element type of q, k, v: GDN_F32 or GDN_BF16                */
+  int32_t o_dtype; /* element type of o: GDN_F32 or GDN_BF16                      */
+  uint32_t flags;  /* GDN_QK_L2NORM                                               */
+} gdn_shape;
+
+/*
+ * Built kernel set (anything else returns GDN_ERR_UNSUPPORTED):
+ *   chunked paths:  dtype GDN_BF16 with d_k = 128, chunk = 64, d_v in {32, 64, 96, 128};
+ *                   dtype GDN_F32  with d_k = 16,  chunk = 16, d_v in {16, 32, ..., 128}.
+ *   decode step:    d_k in {16, 128}, d_v in {16, 128}, either dtype.
+ */
+
+/*
+ * gdn_chunk_fwd: the chunked prompt path (the pages' "prompt's chunked" kernel).
+ *
+ *   q, k           [B, T, H_qk, d_k]  dtype
+ *   v              [B, T, H_v, d_v]   dtype
+ *   g, beta        [B, T, H_v]        float32; g is a log decay (<= 0, -inf
+ *                                     resets the state), beta the write strength
+ *   initial_state  [N, H_v, d_k, d_v] float32, or NULL for a zero state
+ *   cu_seqlens     int32 [N+1] on the device, or NULL.  Non-NULL packs N
+ *                  sequences on one row (B == 1): sequence n owns tokens
+ *                  [cu[n], cu[n+1]), no state crosses a boundary (the pages'
+ *                  split-point convention for packed rows).  cu[0] == 0,
+ *                  non-decreasing, cu[N] == T.  A device array violating this
+ *                  makes every kernel of the call a no-op and sets the status
+ *                  word at the start of the workspace to nonzero.
+ *   num_seqs       N when cu_seqlens is given (ignored otherwise; N = B)
+ *   o              [B, T, H_v, d_v]   o_dtype (written)
+ *   final_state    [N, H_v, d_k, d_v] float32, or NULL (not written).  It may be
+ *                  the same pointer as initial_state (in-place continuation of
+ *                  a cache buffer); any other overlap with an input is refused.
+ *   workspace      device scratch of at least gdn_chunk_fwd_workspace() bytes,
+ *                  contents undefined on entry and exit.  It holds the per-chunk
+ *                  triangular factors between the two launches of the call.
+ */
+gdn_status gdn_chunk_fwd(const gdn_shape *s, const void *q, const void *k,
+                         const void *v, const float *g, const float *beta,
+                         const float *initial_state, const int32_t *cu_seqlens,
+                         int32_t num_seqs, void *o, float *final_state,
+                         void *workspace, size_t workspace_bytes,
+                         hipStream_t stream);
+
+/* Workspace bytes gdn_chunk_fwd needs for this shape; num_seqs is N when the
+   call will pass cu_seqlens, else 0.  Returns 0 if the shape is invalid. */
+size_t gdn_chunk_fwd_workspace(const gdn_shape *s, int32_t num_seqs);
+
+/*
+ * gdn_recurrent_step: one decode token per sequence (the pages' "decode step's
+ * recurrent" kernel).  s->T must be 1.
+ *
+ *   q, k    [B, 1, H_qk, d_k]  dtype
+ *   v       [B, 1, H_v, d_v]   dtype
+ *   g, beta [B, 1, H_v]        float32
+ *   state   [B, H_v, d_k, d_v] float32, read and updated IN PLACE
+ *   o       [B, 1, H_v, d_v]   o_dtype (written); must not overlap state
+ */
+gdn_status gdn_recurrent_step(const gdn_shape *s, const void *q, const void *k,
+                              const void *v, const float *g, const float *beta,
+                              float *state, void *o, hipStream_t stream);
+
+/*
+ * gdn_states_fwd: gdn_chunk_fwd plus the state after every token (the pages'
+ * `states`, [batch seq heads key_dim value_dim] float32, produced by their
+ * token-by-token route).
+ *
+ *   states  [B, T, H_v, d_k, d_v] float32 (written); must not overlap any
+ *           other argument.  states[.., t, h] is S after token t of its
+ *           sequence, so the last token's entry equals final_state.
+ * Other arguments as gdn_chunk_fwd; o and final_state may be NULL here.
+ */
+gdn_status gdn_states_fwd(const gdn_shape *s, const void *q, const void *k,
+                          const void *v, const float *g, const float *beta,
+                          const float *initial_state, const int32_t *cu_seqlens,
+                          int32_t num_seqs, void *o, float *states,
+                          float *final_state, void *workspace,
+                          size_t workspace_bytes, hipStream_t stream);
+
+/* Workspace bytes gdn_states_fwd needs (num_seqs as for gdn_chunk_fwd_workspace). */
+size_t gdn_states_fwd_workspace(const gdn_shape *s, int32_t num_seqs);
+
+/* Static text for a status code. */
+const char *gdn_status_string(gdn_status st);
+
+/* Detail of the last failed call on this host thread ("" if none). */
+const char *gdn_last_error(void);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int gdn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H */

@@ -1,0 +1,265 @@
+"""GPU parity of libgdn against the fp64 oracle on sizes the oracle finishes in seconds.
+
+Every call goes through the C ABI (the ctypes binding).  Sizes span several 64-token
+chunks and end in a ragged tail; the edge cases are the method's own: a -inf decay
+(reset), empty sequences, carried state, in-place continuation, other head ratios.
+"""
+import numpy as np
+import pytest
+import torch
+
+from gated_deltanet_linear_amd import synth
+from oracle import gdn_ref
+from parity_util import TOL_BF16_O, TOL_BF16_STATE, TOL_F32, host, rel_fro, rel_max, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _lib():
+    import gated_deltanet_linear_amd as gdn
+    return gdn
+
+
+def _ref(inp, **kw):
+    return gdn_ref.recurrent(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], s0=inp.get("s0"),
+                             cu_seqlens=inp.get("cu_seqlens"), **kw)
+
+
+def test_tiny_fp32_all_outputs():
+    """The tiny fp32 workload: o, final state and every per-token state within 1e-4 RMS."""
+    gdn = _lib()
+    inp = synth.make_inputs(synth.WORKLOADS["tiny_fp32"], seed=0)
+    d = to_dev(inp)
+    ref = _ref(inp, want_states=True)
+    o, fin = gdn.gdn_chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], chunk=16)
+    o2, st, fin2 = gdn.gdn_states_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], chunk=16)
+    torch.cuda.synchronize()
+    assert rel_max(host(o), ref["o"]) <= TOL_F32
+    assert rel_max(host(fin), ref["final"]) <= TOL_F32
+    assert rel_max(host(o2), ref["o"]) <= TOL_F32
+    assert rel_max(host(fin2), ref["final"]) <= TOL_F32
+    assert rel_max(host(st), ref["states"]) <= TOL_F32
+
+
+def test_tiny_fp32_decode_steps_match_oracle():
+    gdn = _lib()
+    inp = synth.make_inputs(synth.WORKLOADS["tiny_fp32"], seed=0)
+    d = to_dev(inp)
+    ref = _ref(inp)
+    state = torch.zeros((1, 2, 16, 16), device="cuda")
+    outs = []
+    for t in range(64):
+        sl = slice(t, t + 1)
+        outs.append(gdn.gdn_recurrent_step(d["q"][:, sl].contiguous(), d["k"][:, sl].contiguous(),
+                                           d["v"][:, sl].contiguous(), d["g"][:, sl].contiguous(),
+                                           d["beta"][:, sl].contiguous(), state))
+    o = torch.cat(outs, dim=1)
+    torch.cuda.synchronize()
+    assert rel_max(host(o), ref["o"]) <= TOL_F32
+    assert rel_max(host(state), ref["final"]) <= TOL_F32
+
+
+def _bf16_case(T=200, seed=3, **kw):
+    w = synth.WORKLOADS["prefill_t4096"]
+    return synth.make_inputs(w, seed=seed, T=T, **kw)
+
+
+@pytest.mark.parametrize("T", [1, 63, 64, 200])
+def test_bf16_ragged_prefill(T):
+    gdn = _lib()
+    inp = _bf16_case(T)
+    d = to_dev(inp)
+    ref = _ref(inp)
+    o, fin = gdn.gdn_chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"])
+    torch.cuda.synchronize()
+    assert rel_max(host(o), ref["o"]) <= TOL_BF16_O
+    assert rel_fro(host(fin), ref["final"]) <= TOL_BF16_STATE
+    # far inside the bound: the products carry fp32-level precision
+    assert rel_max(host(o), ref["o"]) <= 2e-3
+
+
+def test_bf16_slow_decay_and_initial_state():
+    """Kept fraction ~0.99 per token: the carry between chunks dominates."""
+    gdn = _lib()
+    inp = _bf16_case(T=300, seed=4, g_shift=-5.0, s0_std=0.02)
+    d = to_dev(inp)
+    ref = _ref(inp)
+    o, fin = gdn.gdn_chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], initial_state=d["s0"])
+    torch.cuda.synchronize()
+    assert rel_max(host(o), ref["o"]) <= TOL_BF16_O
+    assert rel_fro(host(fin), ref["final"]) <= TOL_BF16_STATE
+
+
+def test_packed_sequences_with_empty_ones():
+    gdn = _lib()
+    w = synth.WORKLOADS["packed_8seq"]
+    lens = (70, 0, 1, 130, 64, 0)
+    inp = synth.make_inputs(w, seed=5, lengths=lens)
+    d = to_dev(inp)
+    ref = _ref(inp)
+    o, fin = gdn.gdn_chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], initial_state=d["s0"],
+                               cu_seqlens=d["cu"])
+    torch.cuda.synchronize()
+    assert rel_max(host(o), ref["o"]) <= TOL_BF16_O
+    assert rel_fro(host(fin), ref["final"]) <= TOL_BF16_STATE
+    # an empty sequence passes its initial state through untouched
+    np.testing.assert_array_equal(host(fin)[1], inp["s0"][1])
+    np.testing.assert_array_equal(host(fin)[5], inp["s0"][5])
+
+
+def test_minus_inf_resets_without_nan():
+    gdn = _lib()
+    inp = _bf16_case(T=150, seed=6, s0_std=0.02)
+    inp["g"][0, 10, :5] = -np.inf       # inside the first chunk
+    inp["g"][0, 64, 5:9] = -np.inf      # first token of the second chunk
+    inp["g"][0, 149, 9:] = -np.inf      # the very last token
+    d = to_dev(inp)
+    ref = _ref(inp)
+    o, fin = gdn.gdn_chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], initial_state=d["s0"])
+    o2, st, fin2 = gdn.gdn_states_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], initial_state=d["s0"])
+    torch.cuda.synchronize()
+    assert torch.isfinite(o).all() and torch.isfinite(fin).all() and torch.isfinite(st).all()
+    assert rel_max(host(o), ref["o"]) <= TOL_BF16_O
+    assert rel_fro(host(fin), ref["final"]) <= TOL_BF16_STATE
+    assert rel_fro(host(fin2), ref["final"]) <= TOL_BF16_STATE
+
+
+def test_l2norm_flag_on_raw_inputs():
+    """The in-kernel l2 norm on un-normalised q, k with norms 0.09 .. 4.1."""
+    gdn = _lib()
+    inp = _bf16_case(T=130, seed=7, normalise=False, raw_norm_range=(0.09, 4.1))
+    d = to_dev(inp)
+    ref = _ref(inp, l2norm=True)
+    o, fin = gdn.gdn_chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], l2norm=True)
+    o2, st, fin2 = gdn.gdn_states_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], l2norm=True)
+    state = torch.zeros((1, 32, 128, 128), device="cuda")
+    for t in range(130):
+        sl = slice(t, t + 1)
+        gdn.gdn_recurrent_step(d["q"][:, sl].contiguous(), d["k"][:, sl].contiguous(),
+                               d["v"][:, sl].contiguous(), d["g"][:, sl].contiguous(),
+                               d["beta"][:, sl].contiguous(), state, l2norm=True)
+    torch.cuda.synchronize()
+    assert rel_max(host(o), ref["o"]) <= TOL_BF16_O
+    assert rel_fro(host(fin), ref["final"]) <= TOL_BF16_STATE
+    assert rel_fro(host(fin2), ref["final"]) <= TOL_BF16_STATE
+    assert rel_fro(host(state), ref["final"]) <= TOL_BF16_STATE
+    # negative control: without the norm the result is far off
+    raw = _ref(inp, l2norm=False)
+    assert rel_fro(raw["final"], ref["final"]) > 0.1
+
+
+def test_split_invariance_and_inplace_continuation():
+    gdn = _lib()
+    inp = _bf16_case(T=230, seed=8, s0_std=0.02)
+    d = to_dev(inp)
+    o_all, fin_all = gdn.gdn_chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], initial_state=d["s0"])
+    T1 = 101                                 # not a multiple of the chunk
+    cache = d["s0"].clone()
+    sl = lambda x, a, b: x[:, a:b].contiguous()
+    o1, _ = gdn.gdn_chunk_fwd(sl(d["q"], 0, T1), sl(d["k"], 0, T1), sl(d["v"], 0, T1), sl(d["g"], 0, T1),
+                              sl(d["beta"], 0, T1), initial_state=cache, final_state=cache)
+    o2, _ = gdn.gdn_chunk_fwd(sl(d["q"], T1, 230), sl(d["k"], T1, 230), sl(d["v"], T1, 230),
+                              sl(d["g"], T1, 230), sl(d["beta"], T1, 230), initial_state=cache,
+                              final_state=cache)
+    torch.cuda.synchronize()
+    ref = _ref(inp)
+    assert rel_max(host(torch.cat([o1, o2], 1)), ref["o"]) <= TOL_BF16_O
+    assert rel_fro(host(cache), ref["final"]) <= TOL_BF16_STATE
+    assert rel_fro(host(cache), host(fin_all)) <= 1e-5
+
+
+@pytest.mark.parametrize("H_qk,H_v", [(4, 4), (2, 6)])
+def test_other_head_ratios(H_qk, H_v):
+    gdn = _lib()
+    w = synth.Workload("ratio", 2, 100, H_qk, H_v, 128, 128, 64, "bf16", 2.0, 0.02)
+    inp = synth.make_inputs(w, seed=9)
+    d = to_dev(inp)
+    ref = _ref(inp)
+    o, fin = gdn.gdn_chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], initial_state=d["s0"])
+    torch.cuda.synchronize()
+    assert rel_max(host(o), ref["o"]) <= TOL_BF16_O
+    assert rel_fro(host(fin), ref["final"]) <= TOL_BF16_STATE
+
+
+def test_chunk_equals_repeated_decode_steps():
+    """Cross-kernel: T decode steps from the same state give the chunked result."""
+    gdn = _lib()
+    inp = _bf16_case(T=70, seed=10, s0_std=0.02)
+    d = to_dev(inp)
+    o, fin = gdn.gdn_chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], initial_state=d["s0"])
+    state = d["s0"].clone()
+    outs = []
+    for t in range(70):
+        sl = slice(t, t + 1)
+        outs.append(gdn.gdn_recurrent_step(d["q"][:, sl].contiguous(), d["k"][:, sl].contiguous(),
+                                           d["v"][:, sl].contiguous(), d["g"][:, sl].contiguous(),
+                                           d["beta"][:, sl].contiguous(), state))
+    torch.cuda.synchronize()
+    ref = _ref(inp)
+    od = torch.cat(outs, 1)
+    assert rel_max(host(od), ref["o"]) <= 1e-4          # the step is fp32 throughout
+    assert rel_fro(host(state), ref["final"]) <= 1e-5
+    assert rel_max(host(o), host(od)) <= TOL_BF16_O
+    assert rel_fro(host(fin), host(state)) <= TOL_BF16_STATE
+
+
+def test_states_match_oracle_and_final():
+    gdn = _lib()
+    inp = _bf16_case(T=150, seed=11, s0_std=0.02)
+    d = to_dev(inp)
+    heads = [0, 17, 31]
+    ref = _ref(inp, heads=heads, want_states=True)
+    o, st, fin = gdn.gdn_states_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], initial_state=d["s0"])
+    torch.cuda.synchronize()
+    sth = host(st[:, :, heads])
+    assert rel_fro(sth, ref["states"]) <= TOL_BF16_STATE
+    assert rel_max(host(o)[:, :, heads], ref["o"][:, :, heads]) <= TOL_BF16_O
+    assert rel_fro(host(st[:, -1]), host(fin)) <= 1e-5
+
+
+def test_empty_prompt_passes_state_through():
+    gdn = _lib()
+    inp = _bf16_case(T=0, seed=12, s0_std=0.02)
+    d = to_dev(inp)
+    o, fin = gdn.gdn_chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], initial_state=d["s0"])
+    torch.cuda.synchronize()
+    assert o.numel() == 0
+    np.testing.assert_array_equal(host(fin), inp["s0"])
+
+
+def test_bitwise_deterministic():
+    gdn = _lib()
+    inp = _bf16_case(T=257, seed=13)
+    d = to_dev(inp)
+    a = gdn.gdn_chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"])
+    b = gdn.gdn_chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"])
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+def test_bf16_output_dtype():
+    gdn = _lib()
+    inp = _bf16_case(T=90, seed=14)
+    d = to_dev(inp)
+    o, _ = gdn.gdn_chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], o_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    ref = _ref(inp)["o"]
+    ref_b = torch.from_numpy(ref.astype(np.float32)).to(torch.bfloat16).float().numpy()
+    # one bf16 rounding of the output on top of the fp32-level error
+    assert rel_max(host(o), ref_b) <= 1e-2
+
+
+def test_bad_cu_seqlens_makes_the_call_a_noop():
+    gdn = _lib()
+    from gated_deltanet_linear_amd import binding
+    inp = synth.make_inputs(synth.WORKLOADS["packed_8seq"], seed=15, lengths=(20, 30))
+    d = to_dev(inp)
+    bad = torch.tensor([0, 40, 30], dtype=torch.int32, device="cuda")   # decreasing
+    s = binding._shape(d["q"], d["v"], None, None, False, torch.float32, 1, 50)
+    ws = torch.zeros(binding.gdn_chunk_fwd_workspace(s, 2), dtype=torch.uint8, device="cuda")
+    o = torch.full((1, 50, 32, 128), 7.0, device="cuda")
+    gdn.gdn_chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], cu_seqlens=bad, o=o, workspace=ws,
+                      output_final_state=False)
+    torch.cuda.synchronize()
+    assert binding.plan_status(ws) != 0
+    assert torch.all(o == 7.0)
