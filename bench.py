@@ -1,0 +1,313 @@
+#!/usr/bin/env python3
+"""Benchmark of libgdn on one MI355X: the gated delta rule's prompt, decode and states paths.
+
+A step is one gdn_chunk_fwd call over the 4096-token single-layer prefill (B=1, 16
+query/key heads over 32 value heads, width 128, bf16 q/k/v, fp32 g/beta/state/o, chunk
+64): the whole chunked hot path, input in HBM, output o and final state written.  The
+headline `value` is its token throughput.  The same JSON line also carries, each with its
+own roofline, the decode step (256 sequences, 1000 consecutive in-place steps), the packed
+8-sequence prefill (49,802 tokens) and the per-token states readout (2048 tokens, 4 GiB of
+fp32 states), and the fp64 CPU oracle timed on the host beside it.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--headline-only] [--no-cpu]
+"""
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
+N_SETS = 3                      # independent input/output sets rotated per step (cold reads)
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--decode-steps", type=int, default=1000)
+    ap.add_argument("--headline-only", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    return ap.parse_args()
+
+
+class Prepared:
+    """One chunked call with every pointer and the workspace bound once, so the timed
+    loop issues the C call directly (no per-call tensor checks)."""
+
+    def __init__(self, lib, fn, shape, args):
+        self.lib, self.fn, self.shape, self.args = lib, fn, shape, args
+
+    def __call__(self):
+        st = self.fn(ctypes.byref(self.shape), *self.args)
+        if st != 0:
+            raise RuntimeError(self.lib.gdn_last_error().decode())
+
+
+def prepare_chunk(lib, b, d, states=False):
+    """Bind a gdn_chunk_fwd (or gdn_states_fwd) call on device inputs d."""
+    import torch
+    P = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())
+    B, T, H_qk, d_k = d["q"].shape
+    H_v, d_v = d["v"].shape[-2:]
+    N = B if d["cu"] is None else d["cu"].numel() - 1
+    s = b.GdnShape(B, T, H_qk, H_v, d_k, d_v, 64, d_k ** -0.5, b.GDN_BF16, b.GDN_F32, 0)
+    nseq = 0 if d["cu"] is None else N
+    dev = d["q"].device
+    o = torch.empty((B, T, H_v, d_v), dtype=torch.float32, device=dev)
+    fin = torch.empty((N, H_v, d_k, d_v), dtype=torch.float32, device=dev)
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    if states:
+        need = lib.gdn_states_fwd_workspace(ctypes.byref(s), nseq)
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
+        st = torch.empty((B, T, H_v, d_k, d_v), dtype=torch.float32, device=dev)
+        args = [P(d["q"]), P(d["k"]), P(d["v"]), P(d["g"]), P(d["beta"]), P(d["s0"]), P(d["cu"]), nseq,
+                P(o), P(st), P(fin), P(ws), need, stream]
+        keep = (o, fin, ws, st)
+        fn = lib.gdn_states_fwd
+    else:
+        need = lib.gdn_chunk_fwd_workspace(ctypes.byref(s), nseq)
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
+        args = [P(d["q"]), P(d["k"]), P(d["v"]), P(d["g"]), P(d["beta"]), P(d["s0"]), P(d["cu"]), nseq,
+                P(o), P(fin), P(ws), need, stream]
+        keep = (o, fin, ws)
+        fn = lib.gdn_chunk_fwd
+    call = Prepared(lib, fn, s, args)
+    call.keep = keep + (d,)   # the C call holds raw pointers: keep every tensor alive
+    return call
+
+
+def timed_chunk_calls(lib, calls, steps, warmup, n_kernels):
+    """Warm up, then time `steps` calls (rotating over `calls`) with the host clock between
+    synchronisations, and each kernel of every timed call with HIP events recorded on the
+    launch stream by the library's timing hook.  Returns (ms per call, [ms per kernel])."""
+    import torch
+    for i in range(warmup):
+        calls[i % len(calls)]()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_kernels + 1)] for _ in range(steps)]
+    for row in evs:          # torch creates an event's handle at its first record
+        for e in row:
+            e.record()
+    torch.cuda.synchronize()
+    arrays = [(ctypes.c_void_p * (n_kernels + 1))(*[ctypes.c_void_p(e.cuda_event) for e in row])
+              for row in evs]
+    assert all(e.cuda_event for row in evs for e in row)
+    t0 = time.perf_counter()
+    for i in range(steps):
+        lib.gdn_set_timing_events(arrays[i], n_kernels + 1)
+        calls[i % len(calls)]()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    lib.gdn_set_timing_events(None, 0)
+    per_kernel = [sum(row[j].elapsed_time(row[j + 1]) for row in evs) / steps for j in range(n_kernels)]
+    return (t1 - t0) * 1e3 / steps, per_kernel
+
+
+def roofline(bound, achieved, peak, unit, traffic=None, **extra):
+    r = {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+         "frac": round(achieved / peak, 4), "traffic": traffic}
+    r.update(extra)
+    return r
+
+
+def chunk_work(tokens, H_v, d_k=128, d_v=128, C=64):
+    """Algorithmic work of the chunked path per token and value head (method's own count):
+    6 d_k d_v (state terms) + C (3 d_k + 2 d_v) (intra-chunk products) + C^2/3 (solve) FLOP;
+    bytes: q, k at query/key-head width (128 + 128), v 256, o fp32 512, g and beta 4 + 4."""
+    flop = 6 * d_k * d_v + C * (3 * d_k + 2 * d_v) + C * C / 3
+    carry_flop = 6 * d_k * d_v + 2 * C * d_v   # the carry kernel's share: state terms, T X, P U
+    nbytes = 128 + 128 + 256 + 512 + 4 + 4
+    carry_bytes = 128 + 128 + 256 + 512
+    th = tokens * H_v
+    return flop * th, nbytes * th, carry_flop * th, carry_bytes * th
+
+
+def bench_prefill(lib, b, synth, to_dev, steps, warmup):
+    w = synth.WORKLOADS["prefill_t4096"]
+    calls = []
+    for s in range(N_SETS):
+        calls.append(prepare_chunk(lib, b, to_dev(synth.make_inputs(w, seed=s))))
+    ms, kern = timed_chunk_calls(lib, calls, steps, warmup, 3)
+    tokens = w.B * w.T
+    flop, nbytes, cflop, cbytes = chunk_work(tokens, w.H_v)
+    names = ["plan", "prep", "carry"]
+    dom = max(range(3), key=lambda i: kern[i])
+    return w, ms, dict(zip(names, kern)), names[dom], flop, nbytes, cflop, cbytes
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}, WORLD_SIZE {world}).", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    from gated_deltanet_linear_amd import binding as b
+    from gated_deltanet_linear_amd import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs an MI355X GPU", file=sys.stderr)
+        sys.exit(2)
+    lib = b.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def to_dev(inp):
+        out = {key: torch.from_numpy(np.ascontiguousarray(inp[key])).to(dev, torch.bfloat16)
+               for key in ("q", "k", "v")}
+        for key in ("g", "beta"):
+            out[key] = torch.from_numpy(inp[key]).to(dev)
+        out["s0"] = None if inp["s0"] is None else torch.from_numpy(inp["s0"]).to(dev)
+        out["cu"] = None if inp["cu_seqlens"] is None else torch.from_numpy(inp["cu_seqlens"]).to(dev)
+        return out
+
+    # ---- headline: prefill, T = 4096 -------------------------------------------------
+    log("prefill_t4096: generating inputs and timing")
+    w, ms, kern, dom, flop, nbytes, cflop, cbytes = bench_prefill(lib, b, synth, to_dev, args.steps,
+                                                                  args.warmup)
+    tokens = w.B * w.T
+    value = tokens / (ms / 1e3)
+    kd = kern["carry"]
+    log(f"prefill: {ms * 1e3:.1f} us/step, kernels(us) " +
+        ", ".join(f"{k}={v * 1e3:.1f}" for k, v in kern.items()))
+    rl = roofline("hbm", cbytes / (kd / 1e3) / 1e9, HBM_PEAK_GBS, "GB/s", kernel="carry_kernel",
+                  kernel_us=round(kd * 1e3, 2),
+                  mfma_achieved=round(cflop / (kd / 1e3) / 1e12, 2), mfma_peak=MFMA_BF16_PEAK_TFLOPS,
+                  mfma_frac=round(cflop / (kd / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4))
+    path = {"us_per_call": round(ms * 1e3, 2),
+            "kernel_us": {k: round(v * 1e3, 2) for k, v in kern.items()},
+            "hbm_GBs": round(nbytes / (ms / 1e3) / 1e9, 1),
+            "hbm_frac": round(nbytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+            "mfma_TFLOPs": round(flop / (ms / 1e3) / 1e12, 2),
+            "mfma_frac": round(flop / (ms / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+            "algorithmic_flop": flop, "algorithmic_bytes": nbytes}
+    result = {
+        "metric": "GDN prefill tokens/s + decode steps/s on 1 MI355X; % MFMA/HBM roofline",
+        "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "prefill_t4096", "B": 1, "T": 4096, "H_qk": 16, "H_v": 32, "d_k": 128,
+                   "d_v": 128, "chunk": 64, "inputs": "bf16 q/k/v, fp32 g/beta", "o": "fp32",
+                   "input_sets_rotated": N_SETS},
+        "roofline": rl,
+        "path": path,
+    }
+
+    if not args.headline_only:
+        # ---- decode: 256 sequences, 1000 consecutive steps ---------------------------
+        log("decode_b256: timing 1000 steps")
+        wd = synth.WORKLOADS["decode_b256"]
+        pool = synth.make_decode_pool(wd, seed=0)
+        qp = torch.from_numpy(pool["q"]).to(dev, torch.bfloat16)
+        kp = torch.from_numpy(pool["k"]).to(dev, torch.bfloat16)
+        vp = torch.from_numpy(pool["v"]).to(dev, torch.bfloat16)
+        gp = torch.from_numpy(pool["g"]).to(dev)
+        bp = torch.from_numpy(pool["beta"]).to(dev)
+        state = torch.from_numpy(pool["s0"]).to(dev)
+        o = torch.empty((wd.B, 1, wd.H_v, wd.d_v), dtype=torch.float32, device=dev)
+        s = b.GdnShape(wd.B, 1, wd.H_qk, wd.H_v, 128, 128, 64, 128 ** -0.5, b.GDN_BF16, b.GDN_F32, 0)
+        P = lambda t: ctypes.c_void_p(t.data_ptr())
+        stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+        dargs = [[P(qp[i]), P(kp[i]), P(vp[i]), P(gp[i]), P(bp[i]), P(state), P(o), stream]
+                 for i in range(wd.pool)]
+        for i in range(16):
+            lib.gdn_recurrent_step(ctypes.byref(s), *dargs[i % wd.pool])
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        nsteps = args.decode_steps
+        t0 = time.perf_counter()
+        e0.record()
+        for i in range(nsteps):
+            st = lib.gdn_recurrent_step(ctypes.byref(s), *dargs[i % wd.pool])
+            if st != 0:
+                raise RuntimeError(lib.gdn_last_error().decode())
+        e1.record()
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) / nsteps
+        step_ms = e0.elapsed_time(e1) / nsteps
+        dbytes = 2 * wd.B * wd.H_v * 128 * 128 * 4 + wd.B * (2 * wd.H_qk * 128 * 2 + wd.H_v * 128 * 2 +
+                                                            2 * wd.H_v * 4 + wd.H_v * 128 * 4)
+        result["decode"] = {
+            "workload": "decode_b256", "steps": nsteps, "us_per_step": round(step_ms * 1e3, 2),
+            "wall_us_per_step": round(wall * 1e6, 2),
+            "steps_per_s": round(1e3 / step_ms, 1), "tokens_per_s": round(wd.B * 1e3 / step_ms, 1),
+            "roofline": roofline("hbm", dbytes / (step_ms / 1e3) / 1e9, HBM_PEAK_GBS, "GB/s",
+                                 kernel="step_kernel", algorithmic_bytes=dbytes)}
+        log(f"decode: {step_ms * 1e3:.1f} us/step")
+        del qp, kp, vp, gp, bp, state, o
+
+        # ---- packed prefill: 8 sequences, 49,802 tokens ------------------------------
+        log("packed_8seq: generating inputs and timing")
+        wp = synth.WORKLOADS["packed_8seq"]
+        dp = to_dev(synth.make_inputs(wp, seed=0))
+        callp = prepare_chunk(lib, b, dp)
+        msp, kp_ = timed_chunk_calls(lib, [callp], max(3, args.steps // 4), 2, 3)
+        flop_p, bytes_p, cflop_p, cbytes_p = chunk_work(wp.T, wp.H_v)
+        result["packed"] = {
+            "workload": "packed_8seq", "tokens": wp.T, "us_per_call": round(msp * 1e3, 2),
+            "tokens_per_s": round(wp.T / (msp / 1e3), 1),
+            "kernel_us": {k: round(v * 1e3, 2) for k, v in zip(["plan", "prep", "carry"], kp_)},
+            "roofline": roofline("hbm", cbytes_p / (kp_[2] / 1e3) / 1e9, HBM_PEAK_GBS, "GB/s",
+                                 kernel="carry_kernel",
+                                 mfma_frac=round(cflop_p / (kp_[2] / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)),
+            "path_mfma_frac": round(flop_p / (msp / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+            "path_hbm_frac": round(bytes_p / (msp / 1e3) / 1e9 / HBM_PEAK_GBS, 4)}
+        log(f"packed: {msp * 1e3:.1f} us/call")
+        del dp, callp
+
+        # ---- states readout: T = 2048, 4 GiB of fp32 states --------------------------
+        log("states_t2048: generating inputs and timing")
+        ws_ = synth.WORKLOADS["states_t2048"]
+        dsx = to_dev(synth.make_inputs(ws_, seed=0))
+        calls = prepare_chunk(lib, b, dsx, states=True)
+        mss, ks_ = timed_chunk_calls(lib, [calls], 5, 2, 4)
+        sbytes = ws_.T * ws_.H_v * 128 * 128 * 4
+        result["states"] = {
+            "workload": "states_t2048", "tokens": ws_.T, "us_per_call": round(mss * 1e3, 2),
+            "tokens_per_s": round(ws_.T / (mss / 1e3), 1),
+            "kernel_us": {k: round(v * 1e3, 2) for k, v in zip(["plan", "prep", "carry", "stream"], ks_)},
+            "roofline": roofline("hbm", sbytes / (ks_[3] / 1e3) / 1e9, HBM_PEAK_GBS, "GB/s",
+                                 kernel="stream_kernel", algorithmic_bytes=sbytes),
+            "path_hbm_frac": round((sbytes + ws_.T * ws_.H_v * 1032) / (mss / 1e3) / 1e9 / HBM_PEAK_GBS, 4)}
+        log(f"states: {mss * 1e3:.1f} us/call")
+        del dsx, calls
+
+    # ---- the fp64 CPU oracle on the host, on the same workload -------------------------
+    if not args.no_cpu:
+        from oracle import gdn_ref
+        inp = synth.make_inputs(w, seed=0)
+        nthr = int(os.environ.get("OMP_NUM_THREADS", "0")) or gdn_ref.max_threads()
+        heads = list(range(w.H_v))
+        t0 = time.perf_counter()
+        reps = 0
+        while True:
+            gdn_ref.recurrent(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], heads=heads,
+                              want_final=False, nthreads=nthr)
+            reps += 1
+            if time.perf_counter() - t0 >= 10.0 or reps >= 20:
+                break
+        dt = (time.perf_counter() - t0) / reps
+        result["cpu_baseline"] = {"value": round(tokens / dt, 1), "unit": "tokens/s", "cores": nthr,
+                                  "kind": "oracle",
+                                  "sample": f"prefill_t4096, all 32 value heads x 4096 tokens, "
+                                            f"fp64 recurrence, {reps} repetition(s) of {dt:.2f} s"}
+        log(f"cpu oracle: {dt:.2f} s per prefill on {nthr} threads")
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -37,7 +37,8 @@ class GdnShape(ctypes.Structure):
 
 
 EXPORTS = ("gdn_chunk_fwd", "gdn_chunk_fwd_workspace", "gdn_recurrent_step", "gdn_states_fwd",
-           "gdn_states_fwd_workspace", "gdn_status_string", "gdn_last_error", "gdn_version")
+           "gdn_states_fwd_workspace", "gdn_set_timing_events", "gdn_status_string",
+           "gdn_last_error", "gdn_version")
 
 _lib = None
 
@@ -68,6 +69,8 @@ def load_library(path: Optional[str] = None):
     lib.gdn_last_error.restype = ctypes.c_char_p
     lib.gdn_last_error.argtypes = []
     lib.gdn_version.restype = ctypes.c_int
+    lib.gdn_set_timing_events.restype = ctypes.c_int
+    lib.gdn_set_timing_events.argtypes = [P, ctypes.c_int]
     if path is None:
         _lib = lib
     return lib
@@ -233,3 +236,10 @@ def plan_status(workspace: torch.Tensor) -> int:
     """The device status word a chunked call leaves at the start of its workspace
     (nonzero when the call's cu_seqlens were malformed and every kernel did nothing)."""
     return int(workspace[:4].view(torch.int32).item())
+
+
+def gdn_set_timing_events(events, n: int):
+    """Install (or with events=None remove) the per-kernel timing hook of the chunked calls.
+    ``events`` is a ctypes array of hipEvent_t handles (torch.cuda.Event.cuda_event)."""
+    lib = load_library()
+    _check(lib, lib.gdn_set_timing_events(events, int(n)), "gdn_set_timing_events")

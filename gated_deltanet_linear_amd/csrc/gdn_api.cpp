@@ -15,6 +15,8 @@
 namespace {
 
 thread_local std::string g_last_error;
+thread_local hipEvent_t *g_events = nullptr;
+thread_local int g_n_events = 0;
 
 gdn_status fail(gdn_status st, const char *fmt, ...) {
   char buf[512];
@@ -26,7 +28,20 @@ gdn_status fail(gdn_status st, const char *fmt, ...) {
   return st;
 }
 
-bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+struct Arg {
+  const void *p;
+  const char *name;
+  size_t align;
+};
+
+// Every non-NULL pointer must be aligned to what its kernel reads or writes it with.
+template <size_t N> gdn_status check_alignment(const Arg (&args)[N]) {
+  for (const Arg &a : args)
+    if (a.p && !aligned(a.p, a.align)) return fail(GDN_ERR_ALIGN, "%s is not %zu-byte aligned", a.name, a.align);
+  return GDN_OK;
+}
 
 struct Span {
   uintptr_t lo = 0, hi = 0;  // [lo, hi)
@@ -126,11 +141,15 @@ gdn_status chunked_common(const gdn_shape *s, const void *q, const void *k, cons
   if (!workspace) return fail(GDN_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need.bytes);
   if (workspace_bytes < need.bytes)
     return fail(GDN_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, need.bytes);
-  const void *ptrs[] = {q, k, v, g, beta, initial_state, o, states, final_state, workspace};
-  const char *names[] = {"q", "k", "v", "g", "beta", "initial_state", "o", "states", "final_state", "workspace"};
-  for (int i = 0; i < 10; ++i)
-    if (ptrs[i] && !aligned16(ptrs[i])) return fail(GDN_ERR_ALIGN, "%s is not 16-byte aligned", names[i]);
-  if (cu_seqlens && (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u)) return fail(GDN_ERR_ALIGN, "cu_seqlens");
+  // q, k, v rows are read with 16-byte vector loads, states written with 16-byte
+  // stores, the workspace read as float4; everything else is scalar.
+  const Arg args[] = {{q, "q", 16},           {k, "k", 16},
+                      {v, "v", 16},           {g, "g", 4},
+                      {beta, "beta", 4},      {initial_state, "initial_state", 4},
+                      {cu_seqlens, "cu_seqlens", 4}, {o, "o", esize(p.o_dtype)},
+                      {states, "states", 16}, {final_state, "final_state", 4},
+                      {workspace, "workspace", 16}};
+  if ((st = check_alignment(args)) != GDN_OK) return st;
 
   const Tensors t = spans(p, q, k, v, g, beta, initial_state, cu_seqlens, o, states, final_state, workspace,
                           workspace_bytes);
@@ -164,6 +183,8 @@ gdn_status chunked_common(const gdn_shape *s, const void *q, const void *k, cons
   a.final_state = final_state;
   a.states = states;
   a.ws = gdn::workspace_layout(p, with_states, workspace);
+  a.events = g_events;
+  a.n_events = g_n_events;
   const hipError_t e = gdn::launch_chunk_path(p, a, with_states, stream);
   if (e != hipSuccess) return fail(GDN_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
   g_last_error.clear();
@@ -192,6 +213,13 @@ const char *gdn_status_string(gdn_status st) {
 const char *gdn_last_error(void) { return g_last_error.c_str(); }
 
 int gdn_version(void) { return 100; }
+
+gdn_status gdn_set_timing_events(hipEvent_t *events, int n) {
+  if (n < 0) return fail(GDN_ERR_SHAPE, "n=%d", n);
+  g_events = events;
+  g_n_events = events ? n : 0;
+  return GDN_OK;
+}
 
 static size_t workspace_query(const gdn_shape *s, int32_t num_seqs, bool states) {
   try {
@@ -248,10 +276,11 @@ gdn_status gdn_recurrent_step(const gdn_shape *s, const void *q, const void *k, 
       return fail(GDN_ERR_UNSUPPORTED, "no decode kernel for d_k=%d d_v=%d", p.d_k, p.d_v);
     if (p.B > 0 && (!q || !k || !v || !g || !beta || !state || !o))
       return fail(GDN_ERR_NULL, "q, k, v, g, beta, state and o are required");
-    const void *ptrs[] = {q, k, v, g, beta, state, o};
-    const char *names[] = {"q", "k", "v", "g", "beta", "state", "o"};
-    for (int i = 0; i < 7; ++i)
-      if (ptrs[i] && !aligned16(ptrs[i])) return fail(GDN_ERR_ALIGN, "%s is not 16-byte aligned", names[i]);
+    // The state is read and written as float4, o written 4 elements at a time.
+    const Arg args[] = {{q, "q", esize(p.dtype)}, {k, "k", esize(p.dtype)},   {v, "v", esize(p.dtype)},
+                        {g, "g", 4},              {beta, "beta", 4},          {state, "state", 16},
+                        {o, "o", 4 * esize(p.o_dtype)}};
+    if ((st = check_alignment(args)) != GDN_OK) return st;
     const Tensors t = spans(p, q, k, v, g, beta, nullptr, nullptr, o, nullptr, nullptr, nullptr, 0);
     const Span sst(state, (size_t)p.B * p.H_v * p.d_k * p.d_v * sizeof(float));
     const Span ins[] = {t.q, t.k, t.v, t.g, t.beta};

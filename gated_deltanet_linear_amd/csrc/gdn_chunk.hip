@@ -622,13 +622,20 @@ __global__ __launch_bounds__(256) void stream_kernel(
 // ---------------------------------------------------------------------------
 // host launchers
 // ---------------------------------------------------------------------------
+// Records a.events[i] on the stream when the timing hook asks for it.
+static void mark(const ChunkArgs &a, int i, hipStream_t st) {
+  if (a.events && i < a.n_events) (void)hipEventRecord(a.events[i], st);
+}
+
 template <typename TIn, int DK, int C, int DVB, bool STATES, bool OBF16>
 static hipError_t run_t(const Problem &p, const ChunkArgs &a, hipStream_t st) {
   const Workspace &w = a.ws;
+  mark(a, 0, st);
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(64), 0, st, a.cu, p.N, p.T, p.T_tot, p.C, p.max_chunks,
                      w.status, w.seq_start, w.chunk_first);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  mark(a, 1, st);
   const TIn *q = static_cast<const TIn *>(a.q), *k = static_cast<const TIn *>(a.k),
             *v = static_cast<const TIn *>(a.v);
   if (p.max_chunks > 0 && p.H_qk > 0) {
@@ -637,6 +644,7 @@ static hipError_t run_t(const Problem &p, const ChunkArgs &a, hipStream_t st) {
                        p.H_v, p.scale, p.l2norm ? 1 : 0);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
+  mark(a, 2, st);
   const int units = p.N * p.H_v * (p.d_v / DVB);
   if (units > 0) {
     const int grid = (units + 7) / 8 * 8;
@@ -646,6 +654,7 @@ static hipError_t run_t(const Problem &p, const ChunkArgs &a, hipStream_t st) {
                        grid);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
+  mark(a, 3, st);
   if constexpr (STATES) {
     const int CGn = p.d_v / 4, RB = 256 / CGn;
     const int zb = ceil_div(p.d_k, RB);
@@ -656,6 +665,7 @@ static hipError_t run_t(const Problem &p, const ChunkArgs &a, hipStream_t st) {
                          p.d_k, p.d_v, p.l2norm ? 1 : 0);
       if ((e = hipGetLastError()) != hipSuccess) return e;
     }
+    mark(a, 4, st);
   }
   return hipSuccess;
 }

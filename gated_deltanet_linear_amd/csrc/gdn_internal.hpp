@@ -55,6 +55,8 @@ struct ChunkArgs {
   float *final_state;  // may be null
   float *states;       // states path only
   Workspace ws;
+  hipEvent_t *events = nullptr;  // optional timing hook: recorded around each launch
+  int n_events = 0;
 };
 hipError_t launch_chunk_path(const Problem &p, const ChunkArgs &a, bool states, hipStream_t stream);
 

@@ -30,7 +30,10 @@
  *    nothing.  A failed launch returns GDN_ERR_HIP.  Device faults surface at
  *    the caller's next synchronisation.  No C++ exception crosses this ABI.
  *  - Calls are reentrant; gdn_last_error() is per host thread.
- *  - All pointers must be 16-byte aligned.
+ *  - Alignment: pointers read or written with 16-byte vector accesses must be
+ *    16-byte aligned (chunked paths: q, k, v, states, workspace; decode step:
+ *    state; o of the decode step to 4 elements); every other pointer to its
+ *    element size.  A misaligned pointer returns GDN_ERR_ALIGN.
  */
 #ifndef GDN_H
 #define GDN_H
@@ -153,6 +156,17 @@ gdn_status gdn_states_fwd(const gdn_shape *s, const void *q, const void *k,
 
 /* Workspace bytes gdn_states_fwd needs (num_seqs as for gdn_chunk_fwd_workspace). */
 size_t gdn_states_fwd_workspace(const gdn_shape *s, int32_t num_seqs);
+
+/*
+ * gdn_set_timing_events: benchmark instrumentation.  While `events` is
+ * non-NULL, every gdn_chunk_fwd / gdn_states_fwd call made on this host thread
+ * records events[0] on its stream before its first kernel and events[i] right
+ * after its i-th kernel, for i < n: plan (1), prep (2), carry (3) and, on the
+ * states path, stream (4).  hipEventElapsedTime(events[i-1], events[i]) is then
+ * the duration of kernel i.  The events are owned by the caller; passing NULL
+ * turns the hook off.  Returns GDN_ERR_SHAPE if n < 0.
+ */
+gdn_status gdn_set_timing_events(hipEvent_t *events, int n);
 
 /* Static text for a status code. */
 const char *gdn_status_string(gdn_status st);

@@ -244,9 +244,11 @@ def test_bf16_output_dtype():
     o, _ = gdn.gdn_chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], o_dtype=torch.bfloat16)
     torch.cuda.synchronize()
     ref = _ref(inp)["o"]
-    ref_b = torch.from_numpy(ref.astype(np.float32)).to(torch.bfloat16).float().numpy()
-    # one bf16 rounding of the output on top of the fp32-level error
-    assert rel_max(host(o), ref_b) <= 1e-2
+    # One rounding to bf16 (relative error <= 2^-9) on top of the fp32-level error; where
+    # a value sits on a rounding boundary the two sides may round apart by one ulp.
+    rms = np.sqrt(np.mean(ref * ref))
+    err = np.abs(host(o).astype(np.float64) - ref)
+    assert np.all(err <= 2.0 ** -8 * np.abs(ref) + 2e-3 * rms)
 
 
 def test_bad_cu_seqlens_makes_the_call_a_noop():
