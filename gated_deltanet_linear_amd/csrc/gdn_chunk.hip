@@ -80,27 +80,64 @@ __device__ __forceinline__ int find_seq(const int32_t *chunk_first, int N, int c
 
 // Operand storage of a policy: bf16 path -> uint16_t (computed values as hi/lo
 // pairs), fp32 path -> float (single arrays, exact fp32 MFMA).
+// ---------------------------------------------------------------------------
+// Operand policies.  bf16 path: inputs are bf16 (uint16_t storage) and every
+// computed operand is a bf16 hi/lo pair; fp32 path: fp32 everywhere, exact
+// fp32 MFMA.  Fr<BF> loads one MFMA operand fragment from LDS:
+//   row(): lane l takes row l%16 of a [M][ld] array whose contraction index is
+//          contiguous, contraction slice k0 + 8(l/16) .. (+4(l/16) for fp32);
+//   col(): lane l takes column l%16 of a [K][ld] array (contraction = row
+//          index), the same contraction slice, gathered element by element.
+// A and B fragments of one MFMA use the same slice assignment, so they agree
+// on which contraction index each lane group feeds.
+// ---------------------------------------------------------------------------
 template <typename TIn> struct Pol {
   static constexpr bool BF = std::is_same<TIn, uint16_t>::value;
   using CT = typename std::conditional<BF, uint16_t, float>::type;
-  static constexpr int PAD = BF ? 8 : 4;    // row padding in elements (16 bytes)
+  static constexpr int PAD = BF ? 8 : 4;  // row padding in elements (16 bytes)
   static constexpr int VEC = 16 / sizeof(TIn);
 };
 
-// acc += A[16 x kmax] * B[kmax x 16] for either policy.
-template <bool BF, int K, bool SA, bool SB, typename TA, typename TB>
-__device__ __forceinline__ void tile(f32x4 &acc, const TA *Ah, const TA *Al, int lda, const TB *Bh,
-                                     const TB *Bl, int ldb, int lane, int kmax = K) {
-  if constexpr (BF) {
-    tile_bf16<K, SA, SB>(acc, Ah, Al, lda, Bh, Bl, ldb, lane, kmax);
-  } else {
-    (void)Al;
-    (void)Bl;
-    tile_f32<K>(acc, Ah, lda, Bh, ldb, lane, kmax);
+template <bool BF> struct Fr;
+template <> struct Fr<true> {
+  using T = bf16x8;
+  static constexpr int KS = 32;
+  static __device__ __forceinline__ T row(const uint16_t *base, int ld, int lane, int k0) {
+    return *reinterpret_cast<const bf16x8 *>(base + (lane & 15) * ld + k0 + 8 * (lane >> 4));
   }
-}
+  static __device__ __forceinline__ T col(const uint16_t *base, int ld, int lane, int k0) {
+    const uint16_t *p = base + (k0 + 8 * (lane >> 4)) * ld + (lane & 15);
+    uint4 u;
+    u.x = (uint32_t)p[0] | ((uint32_t)p[ld] << 16);
+    u.y = (uint32_t)p[2 * ld] | ((uint32_t)p[3 * ld] << 16);
+    u.z = (uint32_t)p[4 * ld] | ((uint32_t)p[5 * ld] << 16);
+    u.w = (uint32_t)p[6 * ld] | ((uint32_t)p[7 * ld] << 16);
+    return __builtin_bit_cast(bf16x8, u);
+  }
+  static __device__ __forceinline__ f32x4 mma(const f32x4 &acc, const T &a, const T &b) {
+    return mfma_bf16(a, b, acc);
+  }
+};
+template <> struct Fr<false> {
+  using T = f32x4;
+  static constexpr int KS = 16;
+  static __device__ __forceinline__ T row(const float *base, int ld, int lane, int k0) {
+    return *reinterpret_cast<const f32x4 *>(base + (lane & 15) * ld + k0 + 4 * (lane >> 4));
+  }
+  static __device__ __forceinline__ T col(const float *base, int ld, int lane, int k0) {
+    const float *p = base + (k0 + 4 * (lane >> 4)) * ld + (lane & 15);
+    return f32x4{p[0], p[ld], p[2 * ld], p[3 * ld]};
+  }
+  static __device__ __forceinline__ f32x4 mma(f32x4 acc, const T &a, const T &b) {
+    acc = mfma_f32(a[0], b[0], acc);
+    acc = mfma_f32(a[1], b[1], acc);
+    acc = mfma_f32(a[2], b[2], acc);
+    return mfma_f32(a[3], b[3], acc);
+  }
+};
 
-// Stores 4 fp32 values v[0..3] as consecutive elements at p (hi) and pl (lo).
+// Stores 4 fp32 values as 4 consecutive elements: split into hi at ph and lo
+// at pl (bf16 path) or as they are at ph (fp32 path).
 template <bool BF, typename CT>
 __device__ __forceinline__ void put4(CT *ph, CT *pl, const f32x4 &v) {
   if constexpr (BF) {
@@ -120,22 +157,33 @@ __device__ __forceinline__ void put4(CT *ph, CT *pl, const f32x4 &v) {
   }
 }
 
+// The per-chunk triangular factors in the workspace: for each (chunk, value
+// head) slot, 4*C*C bytes.  bf16 path: a hi plane then a lo plane of C x C
+// bf16 (row-major); fp32 path: one C x C fp32 plane.
+template <typename CT, int C>
+__device__ __forceinline__ CT *plane(unsigned char *base, int64_t slot) {
+  return reinterpret_cast<CT *>(base + slot * (int64_t)(4 * C * C));
+}
+
 // ---------------------------------------------------------------------------
-// prep: per (chunk, query/key head), for each value head of the group.
+// prep: per (chunk, query/key head): K K^T and Q K^T once, then for each value
+// head of the group the decays, A, T = (I + A)^{-1}, T diag(beta) and P.
 // ---------------------------------------------------------------------------
 template <typename TIn, int DK, int C> struct PrepSmem {
   static constexpr int LDQ = DK + Pol<TIn>::PAD;
   static constexpr int LDC = C + 4;
-  alignas(16) TIn q[C * LDQ];
-  alignas(16) TIn k[C * LDQ];
-  alignas(16) float G[C * LDC];   // K K^T (lower tiles)
-  alignas(16) float QK[C * LDC];  // Q K^T (lower tiles)
-  alignas(16) float A[C * LDC];
-  alignas(16) float Tm[C * LDC];
-  alignas(16) float Y[4][16 * 16];
+  static constexpr int QKB = 2 * C * LDQ * (int)sizeof(TIn);
+  static constexpr int TRB = 2 * C * LDC * (int)sizeof(float);
+  static constexpr int UB = QKB > TRB ? QKB : TRB;
+  alignas(16) unsigned char u[UB];  // q, k while loading; A, T once K K^T and Q K^T exist
+  alignas(16) float G[C * LDC];     // K K^T (lower tiles)
+  alignas(16) float QK[C * LDC];    // Q K^T (lower tiles)
   alignas(16) double gam[C];
-  float beta[C];
-  float rq[C], rk[C];
+  float beta[C], rq[C], rk[C];
+  __device__ TIn *q() { return reinterpret_cast<TIn *>(u); }
+  __device__ TIn *k() { return q() + C * LDQ; }
+  __device__ float *A() { return reinterpret_cast<float *>(u); }
+  __device__ float *T() { return A() + C * LDC; }
 };
 
 template <typename TIn, int DK, int C>
@@ -143,12 +191,14 @@ __global__ __launch_bounds__(256) void prep_kernel(
     const TIn *__restrict__ q, const TIn *__restrict__ k, const float *__restrict__ g,
     const float *__restrict__ beta, const int32_t *__restrict__ status,
     const int32_t *__restrict__ seq_start, const int32_t *__restrict__ chunk_first,
-    float *__restrict__ tb, float *__restrict__ pm, float *__restrict__ eg, float *__restrict__ eb,
-    int N, int H_qk, int H_v, float scale, int l2norm) {
+    unsigned char *__restrict__ tbw, unsigned char *__restrict__ pmw, float *__restrict__ eg,
+    float *__restrict__ eb, int N, int H_qk, int H_v, float scale, int l2norm) {
   using P = Pol<TIn>;
+  using F = Fr<P::BF>;
+  using CT = typename P::CT;
   using S = PrepSmem<TIn, DK, C>;
   constexpr int LDQ = S::LDQ, LDC = S::LDC, VEC = P::VEC, VPR = DK / VEC, NB = C / 16;
-  static_assert(C % 16 == 0 && C <= 64 && DK % VEC == 0, "prep tiling");
+  static_assert(C % 16 == 0 && C <= 64 && DK % F::KS == 0, "prep tiling");
   __shared__ S sm;
 
   if (*status) return;
@@ -160,6 +210,7 @@ __global__ __launch_bounds__(256) void prep_kernel(
   const int j = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, lg = lane >> 4;
+  TIn *sq = sm.q(), *sk = sm.k();
 
   // q, k rows of this chunk (zero beyond len).
   for (int x = tid; x < C * VPR; x += 256) {
@@ -170,26 +221,25 @@ __global__ __launch_bounds__(256) void prep_kernel(
       qv = *reinterpret_cast<const uint4 *>(q + off);
       kv = *reinterpret_cast<const uint4 *>(k + off);
     }
-    *reinterpret_cast<uint4 *>(sm.q + r * LDQ + cv * VEC) = qv;
-    *reinterpret_cast<uint4 *>(sm.k + r * LDQ + cv * VEC) = kv;
+    *reinterpret_cast<uint4 *>(sq + r * LDQ + cv * VEC) = qv;
+    *reinterpret_cast<uint4 *>(sk + r * LDQ + cv * VEC) = kv;
   }
   __syncthreads();
-  if (tid < C) {
-    float rq = 1.f, rk = 1.f;
+  if (tid < 2 * C) {
+    const int r = tid % C;
+    float rn = 1.f;
     if (l2norm) {
-      float sq = 0.f, sk = 0.f;
+      const TIn *row = (tid < C ? sq : sk) + r * LDQ;
+      float ss = 0.f;
       for (int i = 0; i < DK; ++i) {
-        const float a = Elem<TIn>::get(sm.q, tid * LDQ + i), b = Elem<TIn>::get(sm.k, tid * LDQ + i);
-        sq += a * a;
-        sk += b * b;
+        const float a = Elem<TIn>::get(row, i);
+        ss += a * a;
       }
-      rq = 1.0f / sqrtf(sq + 1e-6f);
-      rk = 1.0f / sqrtf(sk + 1e-6f);
+      rn = 1.0f / sqrtf(ss + 1e-6f);
     }
-    sm.rq[tid] = rq * scale;
-    sm.rk[tid] = rk;
+    if (tid < C) sm.rq[r] = rn * scale;
+    else sm.rk[r] = rn;
   }
-
   // K K^T and Q K^T: the lower 16x16 tiles (diagonal included) on MFMA.
   constexpr int NTRI = NB * (NB + 1) / 2;
   for (int t = wave; t < 2 * NTRI; t += 4) {
@@ -199,15 +249,17 @@ __global__ __launch_bounds__(256) void prep_kernel(
     while ((mi + 1) * (mi + 2) / 2 <= tt) ++mi;
     const int ni = tt - mi * (mi + 1) / 2;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    const TIn *Ab = (isq ? sm.q : sm.k) + mi * 16 * LDQ;
-    const TIn *Bb = sm.k + ni * 16 * LDQ;
-    tile<P::BF, DK, false, false>(acc, Ab, Ab, LDQ, Bb, Bb, LDQ, lane);
+    const TIn *Ab = (isq ? sq : sk) + mi * 16 * LDQ;
+    const TIn *Bb = sk + ni * 16 * LDQ;
+#pragma unroll
+    for (int k0 = 0; k0 < DK; k0 += F::KS) acc = F::mma(acc, F::row(Ab, LDQ, lane, k0), F::row(Bb, LDQ, lane, k0));
     float *D = isq ? sm.QK : sm.G;
 #pragma unroll
     for (int i = 0; i < 4; ++i) D[(mi * 16 + 4 * lg + i) * LDC + ni * 16 + lr] = acc[i];
   }
-  __syncthreads();
+  __syncthreads();  // q and k are dead from here; their space holds A and T
 
+  float *A = sm.A(), *Tm = sm.T();
   const int R = H_v / H_qk;
   for (int rr = 0; rr < R; ++rr) {
     const int h = j * R + rr;
@@ -226,29 +278,37 @@ __global__ __launch_bounds__(256) void prep_kernel(
       }
     }
     __syncthreads();
-    const double glast = sm.gam[C - 1];
-    for (int x = tid; x < C * C; x += 256) {
-      const int r = x / C, i = x - r * C;
-      float a = 0.f, pv = 0.f;
-      if (i <= r) {
-        const float dec = expf((float)(sm.gam[r] - sm.gam[i]));
-        pv = sm.rq[r] * sm.rk[i] * dec * sm.QK[r * LDC + i];
-        if (i < r) a = sm.beta[r] * dec * sm.rk[r] * sm.rk[i] * sm.G[r * LDC + i];
+    // A (strictly lower) to LDS; P (lower, diagonal included) to the workspace.
+    CT *pph = plane<CT, C>(pmw, slot), *ppl = pph + C * C;
+    for (int x4 = tid; x4 < C * C / 4; x4 += 256) {
+      const int r = (4 * x4) / C, i0 = (4 * x4) % C;
+      f32x4 av, pv;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = i0 + e;
+        float a = 0.f, p = 0.f;
+        if (i <= r) {
+          const float dec = expf((float)(sm.gam[r] - sm.gam[i]));
+          p = sm.rq[r] * sm.rk[i] * dec * sm.QK[r * LDC + i];
+          if (i < r) a = sm.beta[r] * dec * sm.rk[r] * sm.rk[i] * sm.G[r * LDC + i];
+        }
+        av[e] = a;
+        pv[e] = p;
       }
-      sm.A[r * LDC + i] = a;
-      pm[slot * C * C + x] = pv;
+      *reinterpret_cast<f32x4 *>(A + r * LDC + i0) = av;
+      put4<P::BF>(pph + 4 * x4, ppl + 4 * x4, pv);
     }
     if (tid < C) {
       eg[slot * C + tid] = expf((float)sm.gam[tid]);
-      eb[slot * C + tid] = expf((float)(glast - sm.gam[tid]));
+      eb[slot * C + tid] = expf((float)(sm.gam[C - 1] - sm.gam[tid]));
     }
     __syncthreads();
 
     // T = (I + A)^{-1}.  Diagonal 16x16 blocks by forward substitution: lane
-    // 16*b + c owns column c of block b.
+    // 16 b + c owns column c of block b.
     if (wave == 0 && lane < C) {
       const int bb = lane >> 4, cc = lane & 15;
-      const float *Ab = sm.A + (bb * 16) * LDC + bb * 16;
+      const float *Ab = A + (bb * 16) * LDC + bb * 16;
       float col[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -258,66 +318,74 @@ __global__ __launch_bounds__(256) void prep_kernel(
         col[r] = s;
       }
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sm.Tm[(bb * 16 + r) * LDC + bb * 16 + cc] = col[r];
+      for (int r = 0; r < 16; ++r) Tm[(bb * 16 + r) * LDC + bb * 16 + cc] = col[r];
     }
     __syncthreads();
-    // Off-diagonal blocks, nearest the diagonal first:
-    //   T_ij = -T_ii * sum_{m=j}^{i-1} A_im T_mj    (wave w: block row i = d + w)
-    for (int d = 1; d < NB; ++d) {
-      const int ib = d + wave, jb = ib - d;
-      if (ib < NB) {
+    // Below the diagonal, wave j fills block column j from the top down:
+    //   T_ij = -T_ii * Y,  Y = sum_{m=j}^{i-1} A_im T_mj      (fp32 MFMA 16x16x4)
+    // Y's MFMA takes contraction slot l/16 = index 4s + l/16 of step s; the
+    // second product takes index 4(l/16) + s instead, which makes the B operand
+    // of step s this lane's own accumulator element Y[4(l/16) + s][l%16].
+    if (wave < NB - 1) {
+      const int jb = wave;
+      for (int ib = jb + 1; ib < NB; ++ib) {
+        f32x4 y = {0.f, 0.f, 0.f, 0.f};
+        for (int m = jb; m < ib; ++m) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * lg + e;
-          float s = 0.f;
-          for (int m = jb; m < ib; ++m)
-#pragma unroll
-            for (int x = 0; x < 16; ++x)
-              s += sm.A[(ib * 16 + r) * LDC + m * 16 + x] * sm.Tm[(m * 16 + x) * LDC + jb * 16 + lr];
-          sm.Y[wave][r * 16 + lr] = s;
+          for (int s = 0; s < 4; ++s)
+            y = mfma_f32(A[(16 * ib + lr) * LDC + 16 * m + 4 * s + lg],
+                         Tm[(16 * m + 4 * s + lg) * LDC + 16 * jb + lr], y);
         }
-      }
-      __syncthreads();
-      if (ib < NB) {
+        f32x4 t = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * lg + e;
-          float s = 0.f;
+        for (int s = 0; s < 4; ++s) t = mfma_f32(Tm[(16 * ib + lr) * LDC + 16 * ib + 4 * lg + s], y[s], t);
 #pragma unroll
-          for (int x = 0; x < 16; ++x) s += sm.Tm[(ib * 16 + r) * LDC + ib * 16 + x] * sm.Y[wave][x * 16 + lr];
-          sm.Tm[(ib * 16 + r) * LDC + jb * 16 + lr] = -s;
-        }
+        for (int e = 0; e < 4; ++e) Tm[(16 * ib + 4 * lg + e) * LDC + 16 * jb + lr] = -t[e];
       }
-      __syncthreads();
     }
-    for (int x = tid; x < C * C; x += 256) {
-      const int r = x / C, i = x - r * C;
-      tb[slot * C * C + x] = (i <= r) ? sm.Tm[r * LDC + i] * sm.beta[i] : 0.f;
+    __syncthreads();
+    CT *tph = plane<CT, C>(tbw, slot), *tpl = tph + C * C;
+    for (int x4 = tid; x4 < C * C / 4; x4 += 256) {
+      const int r = (4 * x4) / C, i0 = (4 * x4) % C;
+      f32x4 tv;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = i0 + e;
+        tv[e] = (i <= r) ? Tm[r * LDC + i] * sm.beta[i] : 0.f;
+      }
+      put4<P::BF>(tph + 4 * x4, tpl + 4 * x4, tv);
     }
     __syncthreads();
   }
 }
 
 // ---------------------------------------------------------------------------
-// carry: one (sequence, value head, DVB-column block of S) walks its chunks.
+// carry: one (sequence, value head, DVB-column block of S) walks its chunks in
+// order.  8 waves; every chunk's shared operands (q, k, v block, T diag(beta),
+// P, decays) are fetched into registers while the previous chunk computes,
+// then staged in LDS.  Per chunk, three barrier-separated phases:
+//   1. [Q;K] S (waves 0-3: Q row tiles, waves 4-7: K row tiles, all column
+//      tiles each, so A fragments are reused); X = V - e^G (K S) -> LDS
+//   2. U = T diag(beta) X, one output tile per wave -> LDS (U and U'')
+//   3. O = e^G Q S + P U (waves 0-3, from their own Q S);
+//      S <- e^{G_last} S + K^T U'' (every wave its own S tiles; K^T fragments
+//      are gathered from row-major K)
 // ---------------------------------------------------------------------------
 template <typename TIn, int DK, int C, int DVB> struct CarrySmem {
   using CT = typename Pol<TIn>::CT;
   static constexpr bool BF = Pol<TIn>::BF;
   static constexpr int PAD = Pol<TIn>::PAD;
   static constexpr int LDQ = DK + PAD;   // Q, K      [C][LDQ]
-  static constexpr int LDKT = C + PAD;   // K^T       [DK][LDKT]
   static constexpr int LDST = DK + PAD;  // S^T       [DVB][LDST]
   static constexpr int LDX = C + PAD;    // Tb, P     [C][LDX];  X^T, U^T, U2^T [DVB][LDX]
   static constexpr int LO = BF ? 1 : 0;  // lo halves exist only on the bf16 path
   alignas(16) TIn q[C * LDQ];
   alignas(16) TIn k[C * LDQ];
-  alignas(16) TIn kt[DK * LDKT];
-  alignas(16) TIn v[C * DVB];
   alignas(16) CT tbh[C * LDX];
   alignas(16) CT tbl[LO ? C * LDX : 4];
   alignas(16) CT ph[C * LDX];
   alignas(16) CT pl[LO ? C * LDX : 4];
+  alignas(16) TIn v[C * DVB];
   alignas(16) CT sth[DVB * LDST];
   alignas(16) CT stl[LO ? DVB * LDST : 4];
   alignas(16) CT xth[DVB * LDX];
@@ -329,24 +397,135 @@ template <typename TIn, int DK, int C, int DVB> struct CarrySmem {
   alignas(16) float eg[C], eb[C], rq[C], rk[C];
 };
 
+// The 16-byte vectors one chunk brings in, numbered: Q rows, K rows, T diag(beta)
+// planes, P planes, the v block, e^G, e^{G_last - G}.
+template <typename TIn, int DK, int C, int DVB> struct ChunkVecs {
+  using CT = typename Pol<TIn>::CT;
+  static constexpr int EQ = 16 / sizeof(TIn), EC = 16 / sizeof(CT);
+  static constexpr int NPLANES = Pol<TIn>::BF ? 2 : 1;
+  static constexpr int QROW = DK / EQ, VROW = DVB / EQ;
+  static constexpr int NQ = C * QROW, NPL = C * C / EC, NTB = NPLANES * NPL, NVV = C * VROW, NE = C / 4;
+  static constexpr int B_K = NQ, B_TB = 2 * NQ, B_PM = B_TB + NTB, B_V = B_PM + NTB, B_EG = B_V + NVV,
+                       B_EB = B_EG + NE, TOTAL = B_EB + NE;
+};
+
+// Next-chunk prefetch into registers.  Every register slot belongs to one
+// region (Q rows, K rows, the T diag(beta) planes, the P planes, the v block,
+// the decay vectors), so the loads carry no divergent branches: a branch join
+// would make the compiler wait for every load in flight.  Rows past the chunk's
+// length are loaded from row 0 (always valid) and zeroed when stashed.
+template <typename TIn, int DK, int C, int DVB, int NT>
+struct Fetch {
+  using V = ChunkVecs<TIn, DK, C, DVB>;
+  using SM = CarrySmem<TIn, DK, C, DVB>;
+  using CT = typename SM::CT;
+  static constexpr int SQ = (V::NQ + NT - 1) / NT, ST = (V::NTB + NT - 1) / NT, SV = (V::NVV + NT - 1) / NT,
+                       SE = (2 * V::NE + NT - 1) / NT;
+  u32x4 rq[SQ], rk[SQ], rt[ST], rp[ST], rv[SV], re[SE];
+  int len;
+
+  __device__ __forceinline__ void load(const TIn *q, const TIn *k, const TIn *v, const unsigned char *tbw,
+                                       const unsigned char *pmw, const float *egw, const float *ebw, int t0,
+                                       int len_, int64_t slot, int j, int h, int H_qk, int H_v, int d_v,
+                                       int col0, int tid) {
+    len = len_;
+#pragma unroll
+    for (int i = 0; i < SQ; ++i) {
+      const int y = tid + i * NT;
+      if (y < V::NQ) {
+        int row = y / V::QROW;
+        row = row < len ? row : 0;
+        const int64_t off = ((int64_t)(t0 + row) * H_qk + j) * DK + (y % V::QROW) * V::EQ;
+        rq[i] = *reinterpret_cast<const u32x4 *>(q + off);
+        rk[i] = *reinterpret_cast<const u32x4 *>(k + off);
+      }
+    }
+    const u32x4 *tb = reinterpret_cast<const u32x4 *>(tbw + slot * (int64_t)(4 * C * C));
+    const u32x4 *pm = reinterpret_cast<const u32x4 *>(pmw + slot * (int64_t)(4 * C * C));
+#pragma unroll
+    for (int i = 0; i < ST; ++i) {
+      const int y = tid + i * NT;
+      if (y < V::NTB) {
+        rt[i] = tb[y];
+        rp[i] = pm[y];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < SV; ++i) {
+      const int y = tid + i * NT;
+      if (y < V::NVV) {
+        int row = y / V::VROW;
+        row = row < len ? row : 0;
+        rv[i] = *reinterpret_cast<const u32x4 *>(v + ((int64_t)(t0 + row) * H_v + h) * d_v + col0 +
+                                                 (y % V::VROW) * V::EQ);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < SE; ++i) {
+      const int y = tid + i * NT;
+      if (y < 2 * V::NE) {
+        const float *src = (y < V::NE ? egw : ebw) + slot * C;
+        re[i] = reinterpret_cast<const u32x4 *>(src)[y % V::NE];
+      }
+    }
+  }
+
+  __device__ __forceinline__ void stash(SM &sm, int tid) const {
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < SQ; ++i) {
+      const int y = tid + i * NT;
+      if (y < V::NQ) {
+        const int row = y / V::QROW, at = row * SM::LDQ + (y % V::QROW) * V::EQ;
+        *reinterpret_cast<u32x4 *>(sm.q + at) = row < len ? rq[i] : zero;
+        *reinterpret_cast<u32x4 *>(sm.k + at) = row < len ? rk[i] : zero;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < ST; ++i) {
+      const int y = tid + i * NT;
+      if (y < V::NTB) {
+        const int pl = y / V::NPL, w = y % V::NPL;
+        const int at = ((w * V::EC) / C) * SM::LDX + (w * V::EC) % C;
+        *reinterpret_cast<u32x4 *>((pl ? sm.tbl : sm.tbh) + at) = rt[i];
+        *reinterpret_cast<u32x4 *>((pl ? sm.pl : sm.ph) + at) = rp[i];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < SV; ++i) {
+      const int y = tid + i * NT;
+      if (y < V::NVV) {
+        const int row = y / V::VROW;
+        *reinterpret_cast<u32x4 *>(sm.v + row * DVB + (y % V::VROW) * V::EQ) = row < len ? rv[i] : zero;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < SE; ++i) {
+      const int y = tid + i * NT;
+      if (y < 2 * V::NE) *reinterpret_cast<u32x4 *>((y < V::NE ? sm.eg : sm.eb) + 4 * (y % V::NE)) = re[i];
+    }
+  }
+};
+
 template <typename TIn, int DK, int C, int DVB, bool STATES, bool OBF16>
-__global__ __launch_bounds__(256) void carry_kernel(
+__global__ __launch_bounds__(512) void carry_kernel(
     const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__restrict__ v,
     const float *__restrict__ s0, const int32_t *__restrict__ status,
     const int32_t *__restrict__ seq_start, const int32_t *__restrict__ chunk_first,
-    const float *__restrict__ tbw, const float *__restrict__ pmw, const float *__restrict__ egw,
-    const float *__restrict__ ebw, void *__restrict__ o, float *__restrict__ fin,
-    float *__restrict__ uw, float *__restrict__ scw, int N, int H_qk, int H_v, int d_v, float scale,
-    int l2norm, int units, int grid) {
+    const unsigned char *__restrict__ tbw, const unsigned char *__restrict__ pmw,
+    const float *__restrict__ egw, const float *__restrict__ ebw, void *__restrict__ o,
+    float *__restrict__ fin, float *__restrict__ uw, float *__restrict__ scw, int N, int H_qk, int H_v,
+    int d_v, float scale, int l2norm, int units, int grid) {
   using P = Pol<TIn>;
+  using F = Fr<P::BF>;
   using SM = CarrySmem<TIn, DK, C, DVB>;
   using CT = typename SM::CT;
   constexpr bool BF = P::BF;
-  constexpr int LDQ = SM::LDQ, LDKT = SM::LDKT, LDST = SM::LDST, LDX = SM::LDX;
-  constexpr int VEC = P::VEC, VPR = DK / VEC, VPV = DVB / VEC;
-  constexpr int NMT = DK / 16, NNT = DVB / 16, NST = NMT * NNT, SPW = (NST + 3) / 4;
-  constexpr int NRT = C / 16, MTW = (NRT + 3) / 4;
-  static_assert(C % 16 == 0 && DK % 16 == 0 && DVB % 16 == 0 && DVB % VEC == 0, "carry tiling");
+  constexpr int NT = 512, KS = F::KS;
+  constexpr int LDQ = SM::LDQ, LDST = SM::LDST, LDX = SM::LDX;
+  constexpr int NMT = DK / 16, NNT = DVB / 16, NST = NMT * NNT, SPW = (NST + 7) / 8;
+  constexpr int NRT = C / 16;
+  static_assert(C % KS == 0 && DK % KS == 0 && DVB % 16 == 0 && NRT <= 4, "carry tiling");
   __shared__ SM sm;
 
   if (*status) return;
@@ -359,12 +538,12 @@ __global__ __launch_bounds__(256) void carry_kernel(
   const int lr = lane & 15, lg = lane >> 4;
   const int col0 = jb * DVB;
 
-  // This wave's tiles of the S block: tile id wave + 4 s -> (row tile, col tile).
+  // This wave's tiles of the S block: tile id wave + 8 s -> (row tile, col tile).
   f32x4 S[SPW];
 #pragma unroll
   for (int s = 0; s < SPW; ++s) {
     S[s] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const int t = wave + 4 * s;
+    const int t = wave + 8 * s;
     if (t < NST && s0) {
       const int mi = t / NNT, ni = t % NNT;
 #pragma unroll
@@ -375,54 +554,24 @@ __global__ __launch_bounds__(256) void carry_kernel(
 
   const int c_begin = chunk_first[n], c_end = chunk_first[n + 1];
   const int s_begin = seq_start[n], s_end = seq_start[n + 1];
+  Fetch<TIn, DK, C, DVB, NT> pre;
+  if (c_begin < c_end)
+    pre.load(q, k, v, tbw, pmw, egw, ebw, s_begin, min(C, s_end - s_begin), (int64_t)c_begin * H_v + h, j, h,
+             H_qk, H_v, d_v, col0, tid);
+
   for (int c = c_begin; c < c_end; ++c) {
     const int t0 = s_begin + (c - c_begin) * C;
     const int len = min(C, s_end - t0);
     const int64_t slot = (int64_t)c * H_v + h;
     __syncthreads();  // the previous chunk is done with every LDS buffer
-
-    // q, k rows and the transposed k; zero beyond len.
-    for (int x = tid; x < C * VPR; x += 256) {
-      const int r = x / VPR, cv = x % VPR;
-      uint4 qv = {0u, 0u, 0u, 0u}, kv = {0u, 0u, 0u, 0u};
-      if (r < len) {
-        const int64_t off = ((int64_t)(t0 + r) * H_qk + j) * DK + cv * VEC;
-        qv = *reinterpret_cast<const uint4 *>(q + off);
-        kv = *reinterpret_cast<const uint4 *>(k + off);
-      }
-      *reinterpret_cast<uint4 *>(sm.q + r * LDQ + cv * VEC) = qv;
-      *reinterpret_cast<uint4 *>(sm.k + r * LDQ + cv * VEC) = kv;
-      const TIn *ke = reinterpret_cast<const TIn *>(&kv);
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) sm.kt[(cv * VEC + e) * LDKT + r] = ke[e];
+    pre.stash(sm, tid);
+    if (!l2norm && tid < C) {
+      sm.rq[tid] = scale;
+      sm.rk[tid] = 1.f;
     }
-    // v block [C][DVB]
-    for (int x = tid; x < C * VPV; x += 256) {
-      const int r = x / VPV, cv = x % VPV;
-      uint4 vv = {0u, 0u, 0u, 0u};
-      if (r < len) vv = *reinterpret_cast<const uint4 *>(v + ((int64_t)(t0 + r) * H_v + h) * d_v + col0 + cv * VEC);
-      *reinterpret_cast<uint4 *>(sm.v + r * DVB + cv * VEC) = vv;
-    }
-    // T diag(beta) and P from the prep phase, split for MFMA.
-    for (int x = tid; x < C * C / 4; x += 256) {
-      const int r = (4 * x) / C, i = (4 * x) % C;
-      const f32x4 a = *reinterpret_cast<const f32x4 *>(tbw + slot * C * C + 4 * x);
-      const f32x4 b = *reinterpret_cast<const f32x4 *>(pmw + slot * C * C + 4 * x);
-      put4<BF>(sm.tbh + r * LDX + i, sm.tbl + (BF ? r * LDX + i : 0), a);
-      put4<BF>(sm.ph + r * LDX + i, sm.pl + (BF ? r * LDX + i : 0), b);
-    }
-    if (tid < C) {
-      sm.eg[tid] = egw[slot * C + tid];
-      sm.eb[tid] = ebw[slot * C + tid];
-      if (!l2norm) {
-        sm.rq[tid] = scale;
-        sm.rk[tid] = 1.f;
-      }
-    }
-    // S -> S^T (split) for [Q;K] S; the states path also keeps the chunk-start state.
 #pragma unroll
     for (int s = 0; s < SPW; ++s) {
-      const int t = wave + 4 * s;
+      const int t = wave + 8 * s;
       if (t < NST) {
         const int mi = t / NNT, ni = t % NNT;
         const int cn = ni * 16 + lr, rk0 = mi * 16 + 4 * lg;
@@ -434,6 +583,9 @@ __global__ __launch_bounds__(256) void carry_kernel(
       }
     }
     __syncthreads();
+    if (c + 1 < c_end)  // in flight while this chunk computes
+      pre.load(q, k, v, tbw, pmw, egw, ebw, t0 + C, min(C, s_end - t0 - C), slot + H_v, j, h, H_qk, H_v, d_v,
+               col0, tid);
     if (l2norm) {
       if (tid < 2 * C) {
         const int r = tid % C;
@@ -450,28 +602,39 @@ __global__ __launch_bounds__(256) void carry_kernel(
       __syncthreads();
     }
 
-    // [Q;K] S for this wave's chunk row tiles; X = V - e^G * (K S) -> X^T.
-    f32x4 qsc[MTW][NNT];
+    // Phase 1: [Q;K] S.  Waves 0-3 take Q row tiles, waves 4-7 K row tiles.
+    const bool isq = wave < 4;
+    const int mt = wave & 3;
+    f32x4 qsc[NNT];
+    if (mt < NRT) {
+      f32x4 acc[NNT];
 #pragma unroll
-    for (int w = 0; w < MTW; ++w) {
-      const int mt = wave + 4 * w;
-      if (mt < NRT) {
+      for (int ni = 0; ni < NNT; ++ni) acc[ni] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const TIn *Ab = (isq ? sm.q : sm.k) + mt * 16 * LDQ;
+#pragma unroll
+      for (int k0 = 0; k0 < DK; k0 += KS) {
+        const auto a = F::row(Ab, LDQ, lane, k0);
 #pragma unroll
         for (int ni = 0; ni < NNT; ++ni) {
-          f32x4 qa = {0.f, 0.f, 0.f, 0.f}, ka = {0.f, 0.f, 0.f, 0.f};
-          const CT *bh = sm.sth + ni * 16 * LDST;
-          const CT *bl = sm.stl + (BF ? ni * 16 * LDST : 0);
-          tile<BF, DK, false, true>(qa, sm.q + mt * 16 * LDQ, sm.q, LDQ, bh, bl, LDST, lane);
-          tile<BF, DK, false, true>(ka, sm.k + mt * 16 * LDQ, sm.k, LDQ, bh, bl, LDST, lane);
+          acc[ni] = F::mma(acc[ni], a, F::row(sm.sth + ni * 16 * LDST, LDST, lane, k0));
+          if constexpr (BF) acc[ni] = F::mma(acc[ni], a, F::row(sm.stl + ni * 16 * LDST, LDST, lane, k0));
+        }
+      }
+#pragma unroll
+      for (int ni = 0; ni < NNT; ++ni) {
+        if (isq) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int r = mt * 16 + 4 * lg + i;
+            qsc[ni][i] = acc[ni][i] * sm.eg[r] * sm.rq[r];
+          }
+        } else {
           f32x4 xv;
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int r = mt * 16 + 4 * lg + i;
-            const float vr = Elem<TIn>::get(sm.v, r * DVB + ni * 16 + lr);
-            xv[i] = vr - sm.eg[r] * sm.rk[r] * ka[i];
-            qa[i] *= sm.eg[r] * sm.rq[r];
+            xv[i] = Elem<TIn>::get(sm.v, r * DVB + ni * 16 + lr) - sm.eg[r] * sm.rk[r] * acc[ni][i];
           }
-          qsc[w][ni] = qa;
           const int cn = ni * 16 + lr, r0 = mt * 16 + 4 * lg;
           put4<BF>(sm.xth + cn * LDX + r0, sm.xtl + (BF ? cn * LDX + r0 : 0), xv);
         }
@@ -479,69 +642,88 @@ __global__ __launch_bounds__(256) void carry_kernel(
     }
     __syncthreads();
 
-    // U = T diag(beta) X  (lower triangular: row tile mt needs columns < 16 (mt+1)).
+    // Phase 2: U = T diag(beta) X (lower triangular: row tile m needs columns < 16 (m + 1)).
+    for (int t = wave; t < NRT * NNT; t += 8) {
+      const int um = t / NNT, un = t % NNT;
+      f32x4 ua = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int w = 0; w < MTW; ++w) {
-      const int mt = wave + 4 * w;
-      if (mt < NRT) {
-#pragma unroll
-        for (int ni = 0; ni < NNT; ++ni) {
-          f32x4 ua = {0.f, 0.f, 0.f, 0.f};
-          tile<BF, C, true, true>(ua, sm.tbh + mt * 16 * LDX, sm.tbl + (BF ? mt * 16 * LDX : 0), LDX,
-                                  sm.xth + ni * 16 * LDX, sm.xtl + (BF ? ni * 16 * LDX : 0), LDX, lane,
-                                  16 * (mt + 1));
-          f32x4 u2;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int r = mt * 16 + 4 * lg + i;
-            u2[i] = sm.eb[r] * sm.rk[r] * ua[i];
-            if constexpr (STATES) {
-              if (r < len) uw[((int64_t)(t0 + r) * H_v + h) * d_v + col0 + ni * 16 + lr] = ua[i];
-            }
+      for (int k0 = 0; k0 < C; k0 += KS) {
+        if (k0 < 16 * (um + 1)) {
+          const auto ah = F::row(sm.tbh + um * 16 * LDX, LDX, lane, k0);
+          const auto bh = F::row(sm.xth + un * 16 * LDX, LDX, lane, k0);
+          ua = F::mma(ua, ah, bh);
+          if constexpr (BF) {
+            ua = F::mma(ua, ah, F::row(sm.xtl + un * 16 * LDX, LDX, lane, k0));
+            ua = F::mma(ua, F::row(sm.tbl + um * 16 * LDX, LDX, lane, k0), bh);
           }
-          const int cn = ni * 16 + lr, r0 = mt * 16 + 4 * lg;
-          put4<BF>(sm.uth + cn * LDX + r0, sm.utl + (BF ? cn * LDX + r0 : 0), ua);
-          put4<BF>(sm.u2h + cn * LDX + r0, sm.u2l + (BF ? cn * LDX + r0 : 0), u2);
         }
       }
+      f32x4 u2;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = um * 16 + 4 * lg + i;
+        u2[i] = sm.eb[r] * sm.rk[r] * ua[i];
+        if constexpr (STATES) {
+          if (r < len) uw[((int64_t)(t0 + r) * H_v + h) * d_v + col0 + un * 16 + lr] = ua[i];
+        }
+      }
+      const int cn = un * 16 + lr, r0 = um * 16 + 4 * lg;
+      put4<BF>(sm.uth + cn * LDX + r0, sm.utl + (BF ? cn * LDX + r0 : 0), ua);
+      put4<BF>(sm.u2h + cn * LDX + r0, sm.u2l + (BF ? cn * LDX + r0 : 0), u2);
     }
     __syncthreads();
 
-    // O = e^G Q S + P U -> o (rows < len).
+    // Phase 3a: O = e^G Q S + P U for this wave's Q row tile; rows < len are stored.
+    if (isq && mt < NRT) {
+      f32x4 oa[NNT];
 #pragma unroll
-    for (int w = 0; w < MTW; ++w) {
-      const int mt = wave + 4 * w;
-      if (mt < NRT) {
+      for (int ni = 0; ni < NNT; ++ni) oa[ni] = qsc[ni];
+#pragma unroll
+      for (int k0 = 0; k0 < C; k0 += KS) {
+        if (k0 < 16 * (mt + 1)) {
+          const auto ah = F::row(sm.ph + mt * 16 * LDX, LDX, lane, k0);
+          typename F::T al;
+          if constexpr (BF) al = F::row(sm.pl + mt * 16 * LDX, LDX, lane, k0);
+#pragma unroll
+          for (int ni = 0; ni < NNT; ++ni) {
+            const auto bh = F::row(sm.uth + ni * 16 * LDX, LDX, lane, k0);
+            oa[ni] = F::mma(oa[ni], ah, bh);
+            if constexpr (BF) {
+              oa[ni] = F::mma(oa[ni], ah, F::row(sm.utl + ni * 16 * LDX, LDX, lane, k0));
+              oa[ni] = F::mma(oa[ni], al, bh);
+            }
+          }
+        }
+      }
+      if (o) {
 #pragma unroll
         for (int ni = 0; ni < NNT; ++ni) {
-          f32x4 oa = qsc[w][ni];
-          tile<BF, C, true, true>(oa, sm.ph + mt * 16 * LDX, sm.pl + (BF ? mt * 16 * LDX : 0), LDX,
-                                  sm.uth + ni * 16 * LDX, sm.utl + (BF ? ni * 16 * LDX : 0), LDX, lane,
-                                  16 * (mt + 1));
-          if (o) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int r = mt * 16 + 4 * lg + i;
-              if (r < len) {
-                const int64_t oi = ((int64_t)(t0 + r) * H_v + h) * d_v + col0 + ni * 16 + lr;
-                if constexpr (OBF16) reinterpret_cast<uint16_t *>(o)[oi] = f2bf(oa[i]);
-                else reinterpret_cast<float *>(o)[oi] = oa[i];
-              }
+          for (int i = 0; i < 4; ++i) {
+            const int r = mt * 16 + 4 * lg + i;
+            if (r < len) {
+              const int64_t oi = ((int64_t)(t0 + r) * H_v + h) * d_v + col0 + ni * 16 + lr;
+              if constexpr (OBF16) reinterpret_cast<uint16_t *>(o)[oi] = f2bf(oa[ni][i]);
+              else reinterpret_cast<float *>(o)[oi] = oa[ni][i];
             }
           }
         }
       }
     }
-    // S <- e^{G_last} S + K^T diag(e^{G_last - G}) U.
+    // Phase 3b: S <- e^{G_last} S + K^T diag(e^{G_last - G}) U.
     const float elast = sm.eg[C - 1];
 #pragma unroll
     for (int s = 0; s < SPW; ++s) {
-      const int t = wave + 4 * s;
+      const int t = wave + 8 * s;
       if (t < NST) {
         const int mi = t / NNT, ni = t % NNT;
         S[s] *= elast;
-        tile<BF, C, false, true>(S[s], sm.kt + mi * 16 * LDKT, sm.kt, LDKT, sm.u2h + ni * 16 * LDX,
-                                 sm.u2l + (BF ? ni * 16 * LDX : 0), LDX, lane);
+#pragma unroll
+        for (int k0 = 0; k0 < C; k0 += KS) {
+          const auto a = F::col(sm.k + mi * 16, LDQ, lane, k0);
+          S[s] = F::mma(S[s], a, F::row(sm.u2h + ni * 16 * LDX, LDX, lane, k0));
+          if constexpr (BF) S[s] = F::mma(S[s], a, F::row(sm.u2l + ni * 16 * LDX, LDX, lane, k0));
+        }
       }
     }
   }
@@ -549,7 +731,7 @@ __global__ __launch_bounds__(256) void carry_kernel(
   if (fin) {
 #pragma unroll
     for (int s = 0; s < SPW; ++s) {
-      const int t = wave + 4 * s;
+      const int t = wave + 8 * s;
       if (t < NST) {
         const int mi = t / NNT, ni = t % NNT;
 #pragma unroll
@@ -640,16 +822,18 @@ static hipError_t run_t(const Problem &p, const ChunkArgs &a, hipStream_t st) {
             *v = static_cast<const TIn *>(a.v);
   if (p.max_chunks > 0 && p.H_qk > 0) {
     hipLaunchKernelGGL((prep_kernel<TIn, DK, C>), dim3(p.max_chunks, p.H_qk), dim3(256), 0, st, q, k, a.g,
-                       a.beta, w.status, w.seq_start, w.chunk_first, w.tb, w.pm, w.eg, w.eb, p.N, p.H_qk,
-                       p.H_v, p.scale, p.l2norm ? 1 : 0);
+                       a.beta, w.status, w.seq_start, w.chunk_first, reinterpret_cast<unsigned char *>(w.tb),
+                       reinterpret_cast<unsigned char *>(w.pm), w.eg, w.eb, p.N, p.H_qk, p.H_v, p.scale,
+                       p.l2norm ? 1 : 0);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   mark(a, 2, st);
   const int units = p.N * p.H_v * (p.d_v / DVB);
   if (units > 0) {
     const int grid = (units + 7) / 8 * 8;
-    hipLaunchKernelGGL((carry_kernel<TIn, DK, C, DVB, STATES, OBF16>), dim3(grid), dim3(256), 0, st, q, k, v,
-                       a.s0, w.status, w.seq_start, w.chunk_first, w.tb, w.pm, w.eg, w.eb, a.o,
+    hipLaunchKernelGGL((carry_kernel<TIn, DK, C, DVB, STATES, OBF16>), dim3(grid), dim3(512), 0, st, q, k, v,
+                       a.s0, w.status, w.seq_start, w.chunk_first, reinterpret_cast<const unsigned char *>(w.tb),
+                       reinterpret_cast<const unsigned char *>(w.pm), w.eg, w.eb, a.o,
                        a.final_state, w.u, w.sc, p.N, p.H_qk, p.H_v, p.d_v, p.scale, p.l2norm ? 1 : 0, units,
                        grid);
     if ((e = hipGetLastError()) != hipSuccess) return e;
