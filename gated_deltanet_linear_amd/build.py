@@ -17,13 +17,16 @@ INCLUDE = os.path.join(ROOT, "include")
 OUT = os.path.join(PKG, "libgdn.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
-SOURCES = ["gdn_api.cpp", "gdn_step.hip", "gdn_chunk.hip"]
+SOURCES = ["gdn_api.cpp", "gdn_step.hip", "gdn_chunk.hip", "gdn_wy.hip"]
 
 # Packed-fp32 VALU forms are kept out of the generated code (the compiler would
 # otherwise form v_pk_{add,mul,fma}_f32 from ordinary float code).
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
           f"-I{INCLUDE}", f"-I{CSRC}", "--offload-arch=gfx950",
-          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          # MFMA accumulators in ordinary VGPRs: the kernels post-process every
+          # accumulator with vector ALU code, which would otherwise copy it out of AGPRs
+          "-mllvm", "-amdgpu-mfma-vgpr-form"]
 
 
 def hipcc() -> str:

@@ -142,11 +142,12 @@ gdn_status chunked_common(const gdn_shape *s, const void *q, const void *k, cons
   if (workspace_bytes < need.bytes)
     return fail(GDN_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, need.bytes);
   // q, k, v rows are read with 16-byte vector loads, states written with 16-byte
-  // stores, the workspace read as float4; everything else is scalar.
+  // stores, o written 4 elements at a time, the workspace read as float4;
+  // everything else is scalar.
   const Arg args[] = {{q, "q", 16},           {k, "k", 16},
                       {v, "v", 16},           {g, "g", 4},
                       {beta, "beta", 4},      {initial_state, "initial_state", 4},
-                      {cu_seqlens, "cu_seqlens", 4}, {o, "o", esize(p.o_dtype)},
+                      {cu_seqlens, "cu_seqlens", 4}, {o, "o", 4 * esize(p.o_dtype)},
                       {states, "states", 16}, {final_state, "final_state", 4},
                       {workspace, "workspace", 16}};
   if ((st = check_alignment(args)) != GDN_OK) return st;

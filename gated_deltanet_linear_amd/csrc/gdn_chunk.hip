@@ -67,17 +67,6 @@ __global__ void plan_kernel(const int32_t *__restrict__ cu, int N, int T, int T_
   *status = bad;
 }
 
-// Sequence n owning global chunk c: chunk_first[n] <= c < chunk_first[n+1].
-__device__ __forceinline__ int find_seq(const int32_t *chunk_first, int N, int c) {
-  int lo = 0, hi = N;
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (chunk_first[mid] <= c) lo = mid;
-    else hi = mid;
-  }
-  return lo;
-}
-
 // Operand storage of a policy: bf16 path -> uint16_t (computed values as hi/lo
 // pairs), fp32 path -> float (single arrays, exact fp32 MFMA).
 // ---------------------------------------------------------------------------
@@ -804,20 +793,41 @@ __global__ __launch_bounds__(256) void stream_kernel(
 // ---------------------------------------------------------------------------
 // host launchers
 // ---------------------------------------------------------------------------
-// Records a.events[i] on the stream when the timing hook asks for it.
-static void mark(const ChunkArgs &a, int i, hipStream_t st) {
-  if (a.events && i < a.n_events) (void)hipEventRecord(a.events[i], st);
+hipError_t launch_plan(const Problem &p, const ChunkArgs &a, hipStream_t st) {
+  const Workspace &w = a.ws;
+  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(64), 0, st, a.cu, p.N, p.T, p.T_tot, p.C, p.max_chunks,
+                     w.status, w.seq_start, w.chunk_first);
+  return hipGetLastError();
+}
+
+template <typename TIn, int C>
+static hipError_t stream_t(const Problem &p, const ChunkArgs &a, hipStream_t st) {
+  const Workspace &w = a.ws;
+  const int CGn = p.d_v / 4, RB = 256 / CGn;
+  const int zb = ceil_div(p.d_k, RB);
+  if (p.max_chunks > 0 && p.H_v > 0 && zb > 0) {
+    const size_t shm = sizeof(float) * ((size_t)C * p.d_v + (size_t)C * RB + C);
+    hipLaunchKernelGGL((stream_kernel<TIn, C>), dim3(p.max_chunks, p.H_v, zb), dim3(256), shm, st,
+                       static_cast<const TIn *>(a.k), a.g, w.u, w.sc, w.status, w.seq_start, w.chunk_first,
+                       a.states, p.N, p.H_qk, p.H_v, p.d_k, p.d_v, p.l2norm ? 1 : 0);
+    return hipGetLastError();
+  }
+  return hipSuccess;
+}
+
+hipError_t launch_states_stream(const Problem &p, const ChunkArgs &a, hipStream_t st) {
+  if (p.dtype == GDN_BF16 && p.C == 64) return stream_t<uint16_t, 64>(p, a, st);
+  if (p.dtype == GDN_F32 && p.C == 16) return stream_t<float, 16>(p, a, st);
+  return hipErrorInvalidValue;
 }
 
 template <typename TIn, int DK, int C, int DVB, bool STATES, bool OBF16>
 static hipError_t run_t(const Problem &p, const ChunkArgs &a, hipStream_t st) {
   const Workspace &w = a.ws;
-  mark(a, 0, st);
-  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(64), 0, st, a.cu, p.N, p.T, p.T_tot, p.C, p.max_chunks,
-                     w.status, w.seq_start, w.chunk_first);
-  hipError_t e = hipGetLastError();
+  mark_event(a, 0, st);
+  hipError_t e = launch_plan(p, a, st);
   if (e != hipSuccess) return e;
-  mark(a, 1, st);
+  mark_event(a, 1, st);
   const TIn *q = static_cast<const TIn *>(a.q), *k = static_cast<const TIn *>(a.k),
             *v = static_cast<const TIn *>(a.v);
   if (p.max_chunks > 0 && p.H_qk > 0) {
@@ -827,7 +837,7 @@ static hipError_t run_t(const Problem &p, const ChunkArgs &a, hipStream_t st) {
                        p.l2norm ? 1 : 0);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  mark(a, 2, st);
+  mark_event(a, 2, st);
   const int units = p.N * p.H_v * (p.d_v / DVB);
   if (units > 0) {
     const int grid = (units + 7) / 8 * 8;
@@ -838,18 +848,10 @@ static hipError_t run_t(const Problem &p, const ChunkArgs &a, hipStream_t st) {
                        grid);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  mark(a, 3, st);
+  mark_event(a, 3, st);
   if constexpr (STATES) {
-    const int CGn = p.d_v / 4, RB = 256 / CGn;
-    const int zb = ceil_div(p.d_k, RB);
-    if (p.max_chunks > 0 && p.H_v > 0 && zb > 0) {
-      const size_t shm = sizeof(float) * ((size_t)C * p.d_v + (size_t)C * RB + C);
-      hipLaunchKernelGGL((stream_kernel<TIn, C>), dim3(p.max_chunks, p.H_v, zb), dim3(256), shm, st, k, a.g,
-                         w.u, w.sc, w.status, w.seq_start, w.chunk_first, a.states, p.N, p.H_qk, p.H_v,
-                         p.d_k, p.d_v, p.l2norm ? 1 : 0);
-      if ((e = hipGetLastError()) != hipSuccess) return e;
-    }
-    mark(a, 4, st);
+    if ((e = launch_states_stream(p, a, st)) != hipSuccess) return e;
+    mark_event(a, 4, st);
   }
   return hipSuccess;
 }
@@ -868,7 +870,7 @@ bool chunk_path_supported(const Problem &p) {
 }
 
 hipError_t launch_chunk_path(const Problem &p, const ChunkArgs &a, bool states, hipStream_t st) {
-  if (p.dtype == GDN_BF16 && p.d_k == 128 && p.C == 64) return run_cfg<uint16_t, 128, 64, 32>(p, a, states, st);
+  if (p.dtype == GDN_BF16 && p.d_k == 128 && p.C == 64) return launch_wy_path(p, a, states, st);
   if (p.dtype == GDN_F32 && p.d_k == 16 && p.C == 16) return run_cfg<float, 16, 16, 16>(p, a, states, st);
   return hipErrorInvalidValue;
 }
@@ -885,10 +887,20 @@ Workspace workspace_layout(const Problem &p, bool states, void *base) {
   const size_t ss = take(sizeof(int32_t) * ((size_t)p.N + 1));
   const size_t cf = take(sizeof(int32_t) * ((size_t)p.N + 1));
   const size_t cc = (size_t)p.max_chunks * p.H_v;
-  const size_t tb = take(sizeof(float) * cc * p.C * p.C);
-  const size_t pm = take(sizeof(float) * cc * p.C * p.C);
-  const size_t eg = take(sizeof(float) * cc * p.C);
-  const size_t eb = take(sizeof(float) * cc * p.C);
+  const bool wy = p.dtype == GDN_BF16;
+  size_t tb = 0, pm = 0, eg = 0, eb = 0, wf = 0, pf = 0, uf = 0, fc = 0, kt = 0;
+  if (wy) {
+    wf = take(kWyWBytes * cc);
+    pf = take(kWyPBytes * cc);
+    uf = take(sizeof(float) * cc * p.C * p.d_v);
+    fc = take(sizeof(float) * cc * kWyFac);
+    kt = take(kWyKtBytes * (size_t)p.max_chunks * p.H_qk);
+  } else {
+    tb = take(sizeof(float) * cc * p.C * p.C);
+    pm = take(sizeof(float) * cc * p.C * p.C);
+    eg = take(sizeof(float) * cc * p.C);
+    eb = take(sizeof(float) * cc * p.C);
+  }
   size_t uo = 0, so = 0;
   if (states) {
     uo = take(sizeof(float) * (size_t)p.T_tot * p.H_v * p.d_v);
@@ -900,10 +912,18 @@ Workspace workspace_layout(const Problem &p, bool states, void *base) {
     w.status = reinterpret_cast<int32_t *>(b + st);
     w.seq_start = reinterpret_cast<int32_t *>(b + ss);
     w.chunk_first = reinterpret_cast<int32_t *>(b + cf);
-    w.tb = reinterpret_cast<float *>(b + tb);
-    w.pm = reinterpret_cast<float *>(b + pm);
-    w.eg = reinterpret_cast<float *>(b + eg);
-    w.eb = reinterpret_cast<float *>(b + eb);
+    if (wy) {
+      w.wf = reinterpret_cast<unsigned char *>(b + wf);
+      w.pf = reinterpret_cast<unsigned char *>(b + pf);
+      w.uf = reinterpret_cast<float *>(b + uf);
+      w.fac = reinterpret_cast<float *>(b + fc);
+      w.ktf = reinterpret_cast<unsigned char *>(b + kt);
+    } else {
+      w.tb = reinterpret_cast<float *>(b + tb);
+      w.pm = reinterpret_cast<float *>(b + pm);
+      w.eg = reinterpret_cast<float *>(b + eg);
+      w.eb = reinterpret_cast<float *>(b + eb);
+    }
     if (states) {
       w.u = reinterpret_cast<float *>(b + uo);
       w.sc = reinterpret_cast<float *>(b + so);

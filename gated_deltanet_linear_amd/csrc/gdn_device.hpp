@@ -11,6 +11,7 @@ namespace gdn {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // raw 16-byte vector
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));  // raw 8-byte vector
 
 constexpr int kWave = 64;
 
@@ -124,6 +125,17 @@ __device__ __forceinline__ double wave_inclusive_scan(double x, int lane) {
     if (lane >= off) x += y;
   }
   return x;
+}
+
+// Sequence n owning global chunk c: chunk_first[n] <= c < chunk_first[n+1].
+__device__ __forceinline__ int find_seq(const int32_t *chunk_first, int N, int c) {
+  int lo = 0, hi = N;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (chunk_first[mid] <= c) lo = mid;
+    else hi = mid;
+  }
+  return lo;
 }
 
 // blockIdx -> logical work item, so that runs of consecutive logical items land

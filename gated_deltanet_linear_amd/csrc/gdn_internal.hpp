@@ -31,6 +31,14 @@ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 //   pm          f32 [max_chunks, H_v, C, C]   scale * (decay mask o Q K^T)
 //   eg          f32 [max_chunks, H_v, C]      exp(G_r)          (G: in-chunk cumsum of g)
 //   eb          f32 [max_chunks, H_v, C]      exp(G_last - G_r)
+//   (the fp32 path keeps tb, pm, eg, eb; the bf16 path keeps instead, per
+//    (chunk, value head) slot, the operands of its state carry in MFMA
+//    fragment order -- see gdn_wy.hip)
+//   wf          bf16 [max_chunks, H_v, 32 KiB]   W = T diag(beta e^G) K, hi/lo
+//   pf          bf16 [max_chunks, H_v, 16 KiB]   P, hi/lo
+//   uf          f32  [max_chunks, H_v, C, d_v]   U' = T diag(beta) V
+//   fac         f32  [max_chunks, H_v, 160]      e^G q-norm, e^{G_last - G} k-norm, e^{G_last}
+//   ktf         bf16 [max_chunks, H_qk, 16 KiB]  K^T
 //   (states path only)
 //   u           f32 [T_tot, H_v, d_v]        per-token write vectors
 //   sc          f32 [max_chunks, H_v, d_k, d_v]  state at each chunk start
@@ -39,9 +47,15 @@ struct Workspace {
   int32_t *seq_start = nullptr;
   int32_t *chunk_first = nullptr;
   float *tb = nullptr, *pm = nullptr, *eg = nullptr, *eb = nullptr;
+  unsigned char *wf = nullptr, *pf = nullptr, *ktf = nullptr;
+  float *uf = nullptr, *fac = nullptr;
   float *u = nullptr, *sc = nullptr;
   size_t bytes = 0;
 };
+
+// Per-slot sizes of the bf16 path's carry operands (d_k = 128, C = 64).
+constexpr size_t kWyWBytes = 32768, kWyPBytes = 16384, kWyKtBytes = 16384;
+constexpr int kWyFac = 160;
 
 // Computes the layout; with base == nullptr only `bytes` is meaningful.
 Workspace workspace_layout(const Problem &p, bool states, void *base);
@@ -59,6 +73,16 @@ struct ChunkArgs {
   int n_events = 0;
 };
 hipError_t launch_chunk_path(const Problem &p, const ChunkArgs &a, bool states, hipStream_t stream);
+
+// Pieces shared by the chunked paths (gdn_chunk.hip): the plan kernel, the
+// per-token states stream, and the timing hook.
+hipError_t launch_plan(const Problem &p, const ChunkArgs &a, hipStream_t stream);
+hipError_t launch_states_stream(const Problem &p, const ChunkArgs &a, hipStream_t stream);
+inline void mark_event(const ChunkArgs &a, int i, hipStream_t st) {
+  if (a.events && i < a.n_events) (void)hipEventRecord(a.events[i], st);
+}
+// The bf16 chunked path (gdn_wy.hip): d_k = 128, C = 64.
+hipError_t launch_wy_path(const Problem &p, const ChunkArgs &a, bool states, hipStream_t stream);
 
 // True when a chunked-path kernel is built for this problem.
 bool chunk_path_supported(const Problem &p);

@@ -32,7 +32,7 @@
  *  - Calls are reentrant; gdn_last_error() is per host thread.
  *  - Alignment: pointers read or written with 16-byte vector accesses must be
  *    16-byte aligned (chunked paths: q, k, v, states, workspace; decode step:
- *    state; o of the decode step to 4 elements); every other pointer to its
+ *    state); o to 4 of its elements (every path); every other pointer to its
  *    element size.  A misaligned pointer returns GDN_ERR_ALIGN.
  */
 #ifndef GDN_H
