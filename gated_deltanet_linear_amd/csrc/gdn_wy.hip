@@ -443,51 +443,58 @@ __global__ __launch_bounds__(256) void wy_chain_kernel(
   // vector-memory counter covers only the operand prefetches.
   __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
 
-  // Loads of chunk c's operands, in three groups; each group is reloaded for
-  // the next chunk right after its last use in this one.
-  auto fetch_wq = [&](ChainOps<NB> &op, int c) {
+  // Where chunk c's operands live, for this lane.
+  struct Src {
+    const u32x4 *w, *kt, *p;
+    const uint16_t *q;
+    const f32x4 *u;
+    const float *f;
+  };
+  auto src = [&](int c) {
+    Src a;
     const int64_t slot = (int64_t)h * MC + c;
     const int t0 = s_begin + (c - c_begin) * C;
-    const int len = min(C, s_end - t0);
-    const u32x4 *W4 = reinterpret_cast<const u32x4 *>(wf + slot * kWyWBytes) + w * 8 * 64 + lane;
-#pragma unroll
-    for (int s = 0; s < 4; ++s)
-#pragma unroll
-      for (int pl = 0; pl < 2; ++pl) op.w[s][pl] = W4[(s * 2 + pl) * 64];
-    const int row = min(16 * w + lr, len - 1);  // rows past the length: any valid row
-    const uint16_t *qr = q + ((int64_t)(t0 + row) * H_qk + j) * DK + 4 * lg;
-#pragma unroll
-    for (int s = 0; s < 4; ++s)
-      op.q[s] = cat(*reinterpret_cast<const u32x2 *>(qr + 32 * s), *reinterpret_cast<const u32x2 *>(qr + 32 * s + 16));
+    const int row = min(16 * w + lr, min(C, s_end - t0) - 1);  // rows past the length: any valid row
+    a.w = reinterpret_cast<const u32x4 *>(wf + slot * kWyWBytes) + w * 8 * 64 + lane;
+    a.kt = reinterpret_cast<const u32x4 *>(ktf + ((int64_t)j * MC + c) * kWyKtBytes) + 2 * w * 2 * 64 + lane;
+    a.p = reinterpret_cast<const u32x4 *>(pf + slot * kWyPBytes) + w * 2 * 2 * 64 + lane;
+    a.q = q + ((int64_t)(t0 + row) * H_qk + j) * DK + 4 * lg;
+    a.u = reinterpret_cast<const f32x4 *>(uf + slot * (int64_t)(C * d_v)) + (w * NCT + jb * NB) * 64 + lane;
+    a.f = fac + slot * kWyFac;
+    return a;
   };
-  auto fetch_uf = [&](ChainOps<NB> &op, int c) {
-    const int64_t slot = (int64_t)h * MC + c;
-    const f32x4 *U4 = reinterpret_cast<const f32x4 *>(uf + slot * (int64_t)(C * d_v)) + lane;
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) op.u[nb] = U4[(w * NCT + jb * NB + nb) * 64];
-    const float *F = fac + slot * kWyFac;
-    op.fq = *reinterpret_cast<const f32x4 *>(F + 16 * w + 4 * lg);
-    op.fu = *reinterpret_cast<const f32x4 *>(F + C + 16 * w + 4 * lg);
+  auto load_wq = [&](ChainOps<NB> &op, const Src &a, int s) {
+    op.w[s][0] = a.w[(s * 2 + 0) * 64];
+    op.w[s][1] = a.w[(s * 2 + 1) * 64];
+    op.q[s] = cat(*reinterpret_cast<const u32x2 *>(a.q + 32 * s), *reinterpret_cast<const u32x2 *>(a.q + 32 * s + 16));
   };
-  auto fetch_kp = [&](ChainOps<NB> &op, int c) {
-    const int64_t slot = (int64_t)h * MC + c;
-    const u32x4 *K4 = reinterpret_cast<const u32x4 *>(ktf + ((int64_t)j * MC + c) * kWyKtBytes) + lane;
+  auto load_uf = [&](ChainOps<NB> &op, const Src &a) {
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int st = 0; st < 2; ++st) op.kt[mt][st] = K4[((2 * w + mt) * 2 + st) * 64];
-    const u32x4 *P4 = reinterpret_cast<const u32x4 *>(pf + slot * kWyPBytes) + lane;
+    for (int nb = 0; nb < NB; ++nb) op.u[nb] = a.u[nb * 64];
+    op.fq = *reinterpret_cast<const f32x4 *>(a.f + 16 * w + 4 * lg);
+    op.fu = *reinterpret_cast<const f32x4 *>(a.f + C + 16 * w + 4 * lg);
+    op.el = a.f[2 * C];
+  };
+  auto load_kt = [&](ChainOps<NB> &op, const Src &a, int mt) {
+    op.kt[mt][0] = a.kt[(mt * 2 + 0) * 64];
+    op.kt[mt][1] = a.kt[(mt * 2 + 1) * 64];
+  };
+  auto load_p = [&](ChainOps<NB> &op, const Src &a) {
 #pragma unroll
     for (int st = 0; st < 2; ++st)
 #pragma unroll
-      for (int pl = 0; pl < 2; ++pl) op.p[st][pl] = P4[((w * 2 + st) * 2 + pl) * 64];
-    op.el = fac[slot * kWyFac + 2 * C];
+      for (int pl = 0; pl < 2; ++pl) op.p[st][pl] = a.p[(st * 2 + pl) * 64];
   };
+  // Scheduling groups (instruction classes for __builtin_amdgcn_sched_group_barrier).
+  constexpr int kMFMA = 0x008, kVMR = 0x020, kDSR = 0x100;
 
-  // One chunk; `cn` is the chunk whose operands are loaded behind this one.
+  // One chunk; the operands of chunk `cn` are loaded behind it, each group of
+  // registers right after its last use here, interleaved with the MFMAs so that
+  // the loads stream while the matrix cores work.
   auto chunk = [&](ChainOps<NB> &op, int c, int cn) {
     const int t0 = s_begin + (c - c_begin) * C;
     const int len = min(C, s_end - t0);
+    const Src nx = src(cn);
     // 1. publish this wave's S rows (the B operand of d_k step w)
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
@@ -505,7 +512,7 @@ __global__ __launch_bounds__(256) void wy_chain_kernel(
       }
     }
     __syncthreads();
-    // 2. W S and Q S for token tile w
+    // 2. W S and Q S for token tile w; W and q of the next chunk stream in behind
     f32x4 aw[NB], aq[NB];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) aw[nb] = aq[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -520,8 +527,15 @@ __global__ __launch_bounds__(256) void wy_chain_kernel(
         aq[nb] = mfma_bf16(as_bf(op.q[s]), sh, aq[nb]);
         aq[nb] = mfma_bf16(as_bf(op.q[s]), sl, aq[nb]);
       }
+      load_wq(op, nx, s);
+      __builtin_amdgcn_sched_group_barrier(kDSR, 2 * NB, 0);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        __builtin_amdgcn_sched_group_barrier(kMFMA, NB, 0);
+        __builtin_amdgcn_sched_group_barrier(kVMR, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(kMFMA, NB, 0);
     }
-    fetch_wq(op, cn);
     // 3. U = U' - W S and U'' = diag(e^{G_last - G} k-norm) U; publish both
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
@@ -543,42 +557,53 @@ __global__ __launch_bounds__(256) void wy_chain_kernel(
         }
       }
     }
-    fetch_uf(op, cn);
+    const float el = op.el;
+    load_uf(op, nx);
     __syncthreads();
-    // 4. S <- e^{G_last} S + K^T U'' for this wave's rows, and
-    //    O = e^G q-norm (Q S) + P U for token tile w
+    // 4. S <- e^{G_last} S + K^T U'' for this wave's rows; U', the factors and
+    //    K^T of the next chunk stream in behind
+    bf16x8 bh[NB][2], bl[NB][2];
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      bf16x8 bh[2], bl[2];
+    for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
-        bh[st] = as_bf(cat(u2x[nb][2 * st][0][lane], u2x[nb][2 * st + 1][0][lane]));
-        bl[st] = as_bf(cat(u2x[nb][2 * st][1][lane], u2x[nb][2 * st + 1][1][lane]));
+        bh[nb][st] = as_bf(cat(u2x[nb][2 * st][0][lane], u2x[nb][2 * st + 1][0][lane]));
+        bl[nb][st] = as_bf(cat(u2x[nb][2 * st][1][lane], u2x[nb][2 * st + 1][1][lane]));
       }
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        S[mt][nb] *= op.el;
+    for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        S[mt][nb] *= el;
 #pragma unroll
         for (int st = 0; st < 2; ++st) {
-          S[mt][nb] = mfma_bf16(as_bf(op.kt[mt][st]), bh[st], S[mt][nb]);
-          S[mt][nb] = mfma_bf16(as_bf(op.kt[mt][st]), bl[st], S[mt][nb]);
+          S[mt][nb] = mfma_bf16(as_bf(op.kt[mt][st]), bh[nb][st], S[mt][nb]);
+          S[mt][nb] = mfma_bf16(as_bf(op.kt[mt][st]), bl[nb][st], S[mt][nb]);
         }
       }
+      load_kt(op, nx, mt);
     }
+    __builtin_amdgcn_sched_group_barrier(kDSR, 8 * NB, 0);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      __builtin_amdgcn_sched_group_barrier(kMFMA, NB, 0);
+      if (k == 3 || k == 7) __builtin_amdgcn_sched_group_barrier(kVMR, 2, 0);
+    }
+    //    O = e^G q-norm (Q S) + P U for token tile w; P of the next chunk behind it
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
         if (st <= (w >> 1)) {  // P is lower triangular
-          const bf16x8 bh = as_bf(cat(ux[nb][2 * st][0][lane], ux[nb][2 * st + 1][0][lane]));
-          const bf16x8 bl = as_bf(cat(ux[nb][2 * st][1][lane], ux[nb][2 * st + 1][1][lane]));
-          aq[nb] = mfma_bf16(as_bf(op.p[st][0]), bh, aq[nb]);
-          aq[nb] = mfma_bf16(as_bf(op.p[st][0]), bl, aq[nb]);
-          aq[nb] = mfma_bf16(as_bf(op.p[st][1]), bh, aq[nb]);
+          const bf16x8 bh2 = as_bf(cat(ux[nb][2 * st][0][lane], ux[nb][2 * st + 1][0][lane]));
+          const bf16x8 bl2 = as_bf(cat(ux[nb][2 * st][1][lane], ux[nb][2 * st + 1][1][lane]));
+          aq[nb] = mfma_bf16(as_bf(op.p[st][0]), bh2, aq[nb]);
+          aq[nb] = mfma_bf16(as_bf(op.p[st][0]), bl2, aq[nb]);
+          aq[nb] = mfma_bf16(as_bf(op.p[st][1]), bh2, aq[nb]);
         }
       }
     }
-    fetch_kp(op, cn);
+    load_p(op, nx);
     if (o) {
       // The O tile goes through LDS so that each lane stores 4 consecutive
       // columns of one row: lane l takes row l%16 and columns 4(l/16) + 16 m.
@@ -611,9 +636,15 @@ __global__ __launch_bounds__(256) void wy_chain_kernel(
   // repeat the last chunk (always valid memory) and go unused.
   if (c_begin < c_end) {
     ChainOps<NB> op;
-    fetch_wq(op, c_begin);
-    fetch_uf(op, c_begin);
-    fetch_kp(op, c_begin);
+    {
+      const Src a = src(c_begin);
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4) load_wq(op, a, s4);
+      load_uf(op, a);
+      load_kt(op, a, 0);
+      load_kt(op, a, 1);
+      load_p(op, a);
+    }
     chunk(op, c_begin, min(c_begin + 1, c_end - 1));
     for (int c = c_begin + 1; c < c_end; ++c) chunk(op, c, min(c + 1, c_end - 1));
   }
