@@ -111,8 +111,8 @@ __global__ __launch_bounds__(256) void wy_prep_kernel(
     const float *__restrict__ g, const float *__restrict__ beta, const int32_t *__restrict__ status,
     const int32_t *__restrict__ seq_start, const int32_t *__restrict__ chunk_first,
     unsigned char *__restrict__ wf, unsigned char *__restrict__ pf, float *__restrict__ uf,
-    float *__restrict__ fac, unsigned char *__restrict__ ktf, int N, int H_qk, int H_v, int d_v, int MC,
-    float scale, int l2norm) {
+    float *__restrict__ fac, unsigned char *__restrict__ ktf, unsigned char *__restrict__ qf, int N, int H_qk,
+    int H_v, int d_v, int MC, float scale, int l2norm) {
   __shared__ PrepSmem sm;
   if (*status) return;
   const int c = blockIdx.x;
@@ -158,6 +158,17 @@ __global__ __launch_bounds__(256) void wy_prep_kernel(
     sm.beta[lane] = lane < len ? braw : 0.f;
   }
   __syncthreads();
+  // Q fragments, once per (chunk, query/key head): item (token tile w, d_k step
+  // s, lane) = Q[16w + l%16][{32s + 4g + i, 32s + 16 + 4g + i}].
+  if (h % R == 0) {
+    u32x4 *Q4 = reinterpret_cast<u32x4 *>(qf + ((int64_t)j * MC + c) * kWyQBytes);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int it = tid + 256 * i, ln = it & 63, ws = it >> 6;
+      const uint16_t *row = sq + (16 * (ws >> 2) + (ln & 15)) * LDQ + 32 * (ws & 3) + 4 * (ln >> 4);
+      Q4[it] = cat(*reinterpret_cast<const u32x2 *>(row), *reinterpret_cast<const u32x2 *>(row + 16));
+    }
+  }
   if (tid < 2 * C) {
     const int r = tid % C;
     float rn = 1.f;
@@ -402,7 +413,8 @@ __global__ __launch_bounds__(256) void wy_chain_kernel(
     const uint16_t *__restrict__ q, const float *__restrict__ s0, const int32_t *__restrict__ status,
     const int32_t *__restrict__ seq_start, const int32_t *__restrict__ chunk_first,
     const unsigned char *__restrict__ wf, const unsigned char *__restrict__ pf, const float *__restrict__ uf,
-    const float *__restrict__ fac, const unsigned char *__restrict__ ktf, void *__restrict__ o,
+    const float *__restrict__ fac, const unsigned char *__restrict__ ktf, const unsigned char *__restrict__ qf,
+    void *__restrict__ o,
     float *__restrict__ fin, float *__restrict__ uw, float *__restrict__ scw, int N, int H_qk, int H_v,
     int d_v, int MC, int units, int grid) {
   // S rows and U rows as published by their owner wave, in the owner's lane order.
@@ -445,20 +457,17 @@ __global__ __launch_bounds__(256) void wy_chain_kernel(
 
   // Where chunk c's operands live, for this lane.
   struct Src {
-    const u32x4 *w, *kt, *p;
-    const uint16_t *q;
+    const u32x4 *w, *kt, *p, *q;
     const f32x4 *u;
     const float *f;
   };
   auto src = [&](int c) {
     Src a;
     const int64_t slot = (int64_t)h * MC + c;
-    const int t0 = s_begin + (c - c_begin) * C;
-    const int row = min(16 * w + lr, min(C, s_end - t0) - 1);  // rows past the length: any valid row
     a.w = reinterpret_cast<const u32x4 *>(wf + slot * kWyWBytes) + w * 8 * 64 + lane;
     a.kt = reinterpret_cast<const u32x4 *>(ktf + ((int64_t)j * MC + c) * kWyKtBytes) + 2 * w * 2 * 64 + lane;
     a.p = reinterpret_cast<const u32x4 *>(pf + slot * kWyPBytes) + w * 2 * 2 * 64 + lane;
-    a.q = q + ((int64_t)(t0 + row) * H_qk + j) * DK + 4 * lg;
+    a.q = reinterpret_cast<const u32x4 *>(qf + ((int64_t)j * MC + c) * kWyQBytes) + w * 4 * 64 + lane;
     a.u = reinterpret_cast<const f32x4 *>(uf + slot * (int64_t)(C * d_v)) + (w * NCT + jb * NB) * 64 + lane;
     a.f = fac + slot * kWyFac;
     return a;
@@ -466,7 +475,7 @@ __global__ __launch_bounds__(256) void wy_chain_kernel(
   auto load_wq = [&](ChainOps<NB> &op, const Src &a, int s) {
     op.w[s][0] = a.w[(s * 2 + 0) * 64];
     op.w[s][1] = a.w[(s * 2 + 1) * 64];
-    op.q[s] = cat(*reinterpret_cast<const u32x2 *>(a.q + 32 * s), *reinterpret_cast<const u32x2 *>(a.q + 32 * s + 16));
+    op.q[s] = a.q[s * 64];
   };
   auto load_uf = [&](ChainOps<NB> &op, const Src &a) {
 #pragma unroll
@@ -482,8 +491,9 @@ __global__ __launch_bounds__(256) void wy_chain_kernel(
   auto load_p = [&](ChainOps<NB> &op, const Src &a) {
 #pragma unroll
     for (int st = 0; st < 2; ++st)
+      if (st <= (w >> 1))  // P is lower triangular: token tiles 0, 1 use step 0 only
 #pragma unroll
-      for (int pl = 0; pl < 2; ++pl) op.p[st][pl] = a.p[(st * 2 + pl) * 64];
+        for (int pl = 0; pl < 2; ++pl) op.p[st][pl] = a.p[(st * 2 + pl) * 64];
   };
   // Scheduling groups (instruction classes for __builtin_amdgcn_sched_group_barrier).
   constexpr int kMFMA = 0x008, kVMR = 0x020, kDSR = 0x100;
@@ -530,11 +540,11 @@ __global__ __launch_bounds__(256) void wy_chain_kernel(
       load_wq(op, nx, s);
       __builtin_amdgcn_sched_group_barrier(kDSR, 2 * NB, 0);
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
+      for (int k = 0; k < 3; ++k) {
         __builtin_amdgcn_sched_group_barrier(kMFMA, NB, 0);
         __builtin_amdgcn_sched_group_barrier(kVMR, 1, 0);
       }
-      __builtin_amdgcn_sched_group_barrier(kMFMA, NB, 0);
+      __builtin_amdgcn_sched_group_barrier(kMFMA, 2 * NB, 0);
     }
     // 3. U = U' - W S and U'' = diag(e^{G_last - G} k-norm) U; publish both
 #pragma unroll
@@ -671,8 +681,8 @@ hipError_t run_wy(const Problem &p, const ChunkArgs &a, hipStream_t st) {
                  *v = static_cast<const uint16_t *>(a.v);
   if (p.max_chunks > 0 && p.H_v > 0) {
     hipLaunchKernelGGL(wy_prep_kernel, dim3(p.max_chunks, p.H_v), dim3(256), 0, st, q, k, v, a.g, a.beta,
-                       w.status, w.seq_start, w.chunk_first, w.wf, w.pf, w.uf, w.fac, w.ktf, p.N, p.H_qk,
-                       p.H_v, p.d_v, p.max_chunks, p.scale, p.l2norm ? 1 : 0);
+                       w.status, w.seq_start, w.chunk_first, w.wf, w.pf, w.uf, w.fac, w.ktf, w.qf, p.N,
+                       p.H_qk, p.H_v, p.d_v, p.max_chunks, p.scale, p.l2norm ? 1 : 0);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   mark_event(a, 2, st);
@@ -680,7 +690,7 @@ hipError_t run_wy(const Problem &p, const ChunkArgs &a, hipStream_t st) {
   if (units > 0) {
     const int grid = (units + 7) / 8 * 8;
     hipLaunchKernelGGL((wy_chain_kernel<NB, STATES, OBF16>), dim3(grid), dim3(256), 0, st, q, a.s0, w.status,
-                       w.seq_start, w.chunk_first, w.wf, w.pf, w.uf, w.fac, w.ktf, a.o, a.final_state, w.u,
+                       w.seq_start, w.chunk_first, w.wf, w.pf, w.uf, w.fac, w.ktf, w.qf, a.o, a.final_state, w.u,
                        w.sc, p.N, p.H_qk, p.H_v, p.d_v, p.max_chunks, units, grid);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
@@ -697,8 +707,8 @@ hipError_t run_wy(const Problem &p, const ChunkArgs &a, hipStream_t st) {
 hipError_t launch_wy_path(const Problem &p, const ChunkArgs &a, bool states, hipStream_t st) {
   if (p.d_k != DK || p.C != C || p.d_v % 32 != 0 || p.d_v > 128) return hipErrorInvalidValue;
   const bool ob = p.o_dtype == GDN_BF16;
-  if (states) return ob ? run_wy<2, true, true>(p, a, st) : run_wy<2, true, false>(p, a, st);
-  return ob ? run_wy<2, false, true>(p, a, st) : run_wy<2, false, false>(p, a, st);
+  if (states) return ob ? run_wy<1, true, true>(p, a, st) : run_wy<1, true, false>(p, a, st);
+  return ob ? run_wy<1, false, true>(p, a, st) : run_wy<1, false, false>(p, a, st);
 }
 
 }  // namespace gdn
