@@ -395,282 +395,295 @@ __global__ __launch_bounds__(256) void wy_prep_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// chain: one (sequence, value head, 16 NB-column block of S) per block of 4 waves.
+// chain: one (sequence, value head, 16-column block of S) per block of 8
+// waves.  Waves 0-3 carry the state: wave w keeps rows [32w, 32w + 32) of the
+// S block in registers and forms the write vectors U of token tile [16w, 16w +
+// 16).  Waves 4-7 produce the output: wave 4 + w computes O for token tile w
+// from the published S and U.  Per chunk c:
+//
+//   state waves                          output waves
+//   publish S (bf16 hi/lo) -> sx[c&1]
+//   ---------------------------- barrier 1 ----------------------------
+//   U = U' - W S, U'' -> ux[c&1], u2x
+//   ---------------------------- barrier 2 ----------------------------
+//   S <- e^{G_last} S + K^T U''           O = e^G q-norm (Q S) + P U
+//                                          (from sx[c&1], ux[c&1])
+//
+// sx and ux are double-buffered by chunk parity, so the output waves work on
+// chunk c while the state waves already publish chunk c + 1; u2x is rewritten
+// only after every wave has passed the next barrier.  Every operand that does not depend on S is
+// loaded from the workspace straight into registers, one chunk ahead, each
+// group right after its last use, interleaved with the MFMAs of its phase.
 // ---------------------------------------------------------------------------
-// The operands of one chunk that do not depend on S, held in registers.
-template <int NB> struct ChainOps {
-  u32x4 w[4][2];   // W hi/lo: token tile of this wave, d_k steps 0..3
-  u32x4 q[4];      // q rows of the token tile, d_k steps 0..3
-  u32x4 kt[2][2];  // K^T: this wave's two d_k tiles, token steps 0..1
-  u32x4 p[2][2];   // P hi/lo: token tile of this wave, token steps 0..1
-  f32x4 u[NB];     // U' tiles
-  f32x4 fq, fu;    // e^G q-norm, e^{G_last - G} k-norm for the 4 rows of this lane
+struct StateOps {
+  u32x4 w[4][2];   // W hi/lo of token tile w, d_k steps 0..3
+  u32x4 kt[2][2];  // K^T of this wave's two d_k tiles, token steps 0..1
+  f32x4 u, fu;     // U' tile; e^{G_last - G} k-norm of this lane's 4 rows
   float el;        // e^{G_last}
 };
+struct OutOps {
+  u32x4 q[4];      // Q of token tile w, d_k steps 0..3
+  u32x4 p[2][2];   // P hi/lo of token tile w, token steps 0..1
+  f32x4 fq;        // e^G q-norm of this lane's 4 rows
+};
 
-template <int NB, bool STATES, bool OBF16>
-__global__ __launch_bounds__(256) void wy_chain_kernel(
-    const uint16_t *__restrict__ q, const float *__restrict__ s0, const int32_t *__restrict__ status,
-    const int32_t *__restrict__ seq_start, const int32_t *__restrict__ chunk_first,
-    const unsigned char *__restrict__ wf, const unsigned char *__restrict__ pf, const float *__restrict__ uf,
-    const float *__restrict__ fac, const unsigned char *__restrict__ ktf, const unsigned char *__restrict__ qf,
-    void *__restrict__ o,
+template <bool STATES, bool OBF16>
+__global__ __launch_bounds__(512) void wy_chain_kernel(
+    const float *__restrict__ s0, const int32_t *__restrict__ status, const int32_t *__restrict__ seq_start,
+    const int32_t *__restrict__ chunk_first, const unsigned char *__restrict__ wf,
+    const unsigned char *__restrict__ pf, const float *__restrict__ uf, const float *__restrict__ fac,
+    const unsigned char *__restrict__ ktf, const unsigned char *__restrict__ qf, void *__restrict__ o,
     float *__restrict__ fin, float *__restrict__ uw, float *__restrict__ scw, int N, int H_qk, int H_v,
     int d_v, int MC, int units, int grid) {
-  // S rows and U rows as published by their owner wave, in the owner's lane order.
-  __shared__ u32x4 sx[NB][4][2][64];
-  __shared__ u32x2 ux[NB][4][2][64];
-  __shared__ u32x2 u2x[NB][4][2][64];
-  constexpr int LDO = 16 * NB + 4;  // O tile rows, fp32 (the pad spreads rows over the banks)
+  // S and U as published by their owner wave, in the owner's lane order.
+  // ux and u2x: the two token tiles of token step st side by side, so a reader
+  // takes its 8 contraction indices with one 16-byte load.
+  __shared__ u32x4 sx[2][4][2][64];
+  __shared__ u32x4 ux[2][2][2][64];
+  __shared__ u32x4 u2x[2][2][64];
+  constexpr int LDO = 20;  // O tile rows, fp32 (the pad spreads rows over the banks)
   __shared__ float ot[4][16 * LDO];
   if (*status) return;
   const int u = xcd_remap(blockIdx.x, grid);
   if (u >= units) return;
-  const int NJB = d_v / (16 * NB), NCT = d_v / 16;
-  const int jb = u % NJB, h = (u / NJB) % H_v, n = u / (NJB * H_v);
+  const int NCT = d_v / 16;
+  const int jb = u % NCT, h = (u / NCT) % H_v, n = u / (NCT * H_v);
   const int j = h / (H_v / H_qk);
   const int lane = threadIdx.x & 63;
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int w = wave & 3;
   const int lr = lane & 15, lg = lane >> 4;
-  const int col0 = jb * 16 * NB;
+  const int col0 = jb * 16;
   const int64_t sbase = (int64_t)(n * H_v + h) * DK;
-
-  // S[mt][nb] holds rows 32w + 16mt + 4lg + i, column col0 + 16nb + lr.
-  f32x4 S[2][NB];
-#pragma unroll
-  for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      S[mt][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (s0) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          S[mt][nb][i] = s0[(sbase + 32 * w + 16 * mt + 4 * lg + i) * d_v + col0 + 16 * nb + lr];
-      }
-    }
-
   const int c_begin = chunk_first[n], c_end = chunk_first[n + 1];
   const int s_begin = seq_start[n], s_end = seq_start[n + 1];
-  // Drain the initial-state loads here, so that inside the chunk loop the
-  // vector-memory counter covers only the operand prefetches.
-  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+  const int64_t hslot = (int64_t)h * MC, jslot = (int64_t)j * MC;
+  constexpr int kMFMA = 0x008, kVMR = 0x020, kDSR = 0x100;  // scheduling-group classes
 
-  // Where chunk c's operands live, for this lane.
-  struct Src {
-    const u32x4 *w, *kt, *p, *q;
-    const f32x4 *u;
-    const float *f;
-  };
-  auto src = [&](int c) {
-    Src a;
-    const int64_t slot = (int64_t)h * MC + c;
-    a.w = reinterpret_cast<const u32x4 *>(wf + slot * kWyWBytes) + w * 8 * 64 + lane;
-    a.kt = reinterpret_cast<const u32x4 *>(ktf + ((int64_t)j * MC + c) * kWyKtBytes) + 2 * w * 2 * 64 + lane;
-    a.p = reinterpret_cast<const u32x4 *>(pf + slot * kWyPBytes) + w * 2 * 2 * 64 + lane;
-    a.q = reinterpret_cast<const u32x4 *>(qf + ((int64_t)j * MC + c) * kWyQBytes) + w * 4 * 64 + lane;
-    a.u = reinterpret_cast<const f32x4 *>(uf + slot * (int64_t)(C * d_v)) + (w * NCT + jb * NB) * 64 + lane;
-    a.f = fac + slot * kWyFac;
-    return a;
-  };
-  auto load_wq = [&](ChainOps<NB> &op, const Src &a, int s) {
-    op.w[s][0] = a.w[(s * 2 + 0) * 64];
-    op.w[s][1] = a.w[(s * 2 + 1) * 64];
-    op.q[s] = a.q[s * 64];
-  };
-  auto load_uf = [&](ChainOps<NB> &op, const Src &a) {
+  if (wave < 4) {
+    // ------------------------------ state waves ------------------------------
+    // S[mt] holds rows 32w + 16mt + 4lg + i, column col0 + lr.
+    f32x4 S[2];
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) op.u[nb] = a.u[nb * 64];
-    op.fq = *reinterpret_cast<const f32x4 *>(a.f + 16 * w + 4 * lg);
-    op.fu = *reinterpret_cast<const f32x4 *>(a.f + C + 16 * w + 4 * lg);
-    op.el = a.f[2 * C];
-  };
-  auto load_kt = [&](ChainOps<NB> &op, const Src &a, int mt) {
-    op.kt[mt][0] = a.kt[(mt * 2 + 0) * 64];
-    op.kt[mt][1] = a.kt[(mt * 2 + 1) * 64];
-  };
-  auto load_p = [&](ChainOps<NB> &op, const Src &a) {
+    for (int mt = 0; mt < 2; ++mt) {
+      S[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (s0) {
 #pragma unroll
-    for (int st = 0; st < 2; ++st)
-      if (st <= (w >> 1))  // P is lower triangular: token tiles 0, 1 use step 0 only
-#pragma unroll
-        for (int pl = 0; pl < 2; ++pl) op.p[st][pl] = a.p[(st * 2 + pl) * 64];
-  };
-  // Scheduling groups (instruction classes for __builtin_amdgcn_sched_group_barrier).
-  constexpr int kMFMA = 0x008, kVMR = 0x020, kDSR = 0x100;
-
-  // One chunk; the operands of chunk `cn` are loaded behind it, each group of
-  // registers right after its last use here, interleaved with the MFMAs so that
-  // the loads stream while the matrix cores work.
-  auto chunk = [&](ChainOps<NB> &op, int c, int cn) {
-    const int t0 = s_begin + (c - c_begin) * C;
-    const int len = min(C, s_end - t0);
-    const Src nx = src(cn);
-    // 1. publish this wave's S rows (the B operand of d_k step w)
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      u32x4 hi, lo;
-      split8(S[0][nb], S[1][nb], hi, lo);
-      sx[nb][w][0][lane] = hi;
-      sx[nb][w][1][lane] = lo;
-      if constexpr (STATES) {
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            scw[(((int64_t)c * H_v + h) * DK + 32 * w + 16 * mt + 4 * lg + i) * d_v + col0 + 16 * nb + lr] =
-                S[mt][nb][i];
+        for (int i = 0; i < 4; ++i) S[mt][i] = s0[(sbase + 32 * w + 16 * mt + 4 * lg + i) * d_v + col0 + lr];
       }
     }
-    __syncthreads();
-    // 2. W S and Q S for token tile w; W and q of the next chunk stream in behind
-    f32x4 aw[NB], aq[NB];
+    // Drain the initial-state loads, so that inside the chunk loop the
+    // vector-memory counter covers only the operand prefetches.
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+
+    auto wp = [&](int c) {
+      return reinterpret_cast<const u32x4 *>(wf + (hslot + c) * kWyWBytes) + w * 8 * 64 + lane;
+    };
+    auto kp = [&](int c) {
+      return reinterpret_cast<const u32x4 *>(ktf + (jslot + c) * kWyKtBytes) + 2 * w * 2 * 64 + lane;
+    };
+    auto load_uf = [&](StateOps &op, int c) {
+      op.u = reinterpret_cast<const f32x4 *>(uf + (hslot + c) * (int64_t)(C * d_v))[(w * NCT + jb) * 64 + lane];
+      const float *F = fac + (hslot + c) * kWyFac;
+      op.fu = *reinterpret_cast<const f32x4 *>(F + C + 16 * w + 4 * lg);
+      op.el = F[2 * C];
+    };
+
+    auto chunk = [&](StateOps &op, int c, int cn) {
+      const int t0 = s_begin + (c - c_begin) * C;
+      const int len = min(C, s_end - t0);
+      // 1. publish this wave's S rows (the B operand of d_k step w)
+      {
+        u32x4 hi, lo;
+        split8(S[0], S[1], hi, lo);
+        sx[c & 1][w][0][lane] = hi;
+        sx[c & 1][w][1][lane] = lo;
+        if constexpr (STATES) {
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) aw[nb] = aq[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+          for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        const bf16x8 sh = as_bf(sx[nb][s][0][lane]), sl = as_bf(sx[nb][s][1][lane]);
-        aw[nb] = mfma_bf16(as_bf(op.w[s][0]), sh, aw[nb]);
-        aw[nb] = mfma_bf16(as_bf(op.w[s][0]), sl, aw[nb]);
-        aw[nb] = mfma_bf16(as_bf(op.w[s][1]), sh, aw[nb]);
-        aq[nb] = mfma_bf16(as_bf(op.q[s]), sh, aq[nb]);
-        aq[nb] = mfma_bf16(as_bf(op.q[s]), sl, aq[nb]);
+            for (int i = 0; i < 4; ++i)
+              scw[(((int64_t)c * H_v + h) * DK + 32 * w + 16 * mt + 4 * lg + i) * d_v + col0 + lr] = S[mt][i];
+        }
       }
-      load_wq(op, nx, s);
-      __builtin_amdgcn_sched_group_barrier(kDSR, 2 * NB, 0);
+      __syncthreads();  // 1
+      // 2. U = U' - W S for token tile w (three accumulators: hi*hi, hi*lo, lo*hi)
+      const u32x4 *W4 = wp(cn);
+      f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0, a2 = a0;
 #pragma unroll
-      for (int k = 0; k < 3; ++k) {
-        __builtin_amdgcn_sched_group_barrier(kMFMA, NB, 0);
+      for (int s = 0; s < 4; ++s) {
+        const bf16x8 sh = as_bf(sx[c & 1][s][0][lane]), sl = as_bf(sx[c & 1][s][1][lane]);
+        a0 = mfma_bf16(as_bf(op.w[s][0]), sh, a0);
+        a1 = mfma_bf16(as_bf(op.w[s][0]), sl, a1);
+        a2 = mfma_bf16(as_bf(op.w[s][1]), sh, a2);
+        op.w[s][0] = W4[(s * 2 + 0) * 64];
+        op.w[s][1] = W4[(s * 2 + 1) * 64];
+        __builtin_amdgcn_sched_group_barrier(kDSR, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(kMFMA, 1, 0);
         __builtin_amdgcn_sched_group_barrier(kVMR, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kMFMA, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kVMR, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kMFMA, 1, 0);
       }
-      __builtin_amdgcn_sched_group_barrier(kMFMA, 2 * NB, 0);
-    }
-    // 3. U = U' - W S and U'' = diag(e^{G_last - G} k-norm) U; publish both
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      const f32x4 uv = op.u[nb] - aw[nb];
+      //    U'' = diag(e^{G_last - G} k-norm) U; publish U and U''
+      const f32x4 uv = op.u - (a0 + a1 + a2);
       const f32x4 u2 = uv * op.fu;
-      u32x2 hi, lo;
-      split4(uv, hi, lo);
-      ux[nb][w][0][lane] = hi;
-      ux[nb][w][1][lane] = lo;
-      split4(u2, hi, lo);
-      u2x[nb][w][0][lane] = hi;
-      u2x[nb][w][1][lane] = lo;
-      aq[nb] *= op.fq;
+      {
+        u32x2 hi, lo;
+        split4(uv, hi, lo);
+        reinterpret_cast<u32x2 *>(&ux[c & 1][w >> 1][0][lane])[w & 1] = hi;
+        reinterpret_cast<u32x2 *>(&ux[c & 1][w >> 1][1][lane])[w & 1] = lo;
+        split4(u2, hi, lo);
+        reinterpret_cast<u32x2 *>(&u2x[w >> 1][0][lane])[w & 1] = hi;
+        reinterpret_cast<u32x2 *>(&u2x[w >> 1][1][lane])[w & 1] = lo;
+      }
       if constexpr (STATES) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int r = 16 * w + 4 * lg + i;
-          if (r < len) uw[((int64_t)(t0 + r) * H_v + h) * d_v + col0 + 16 * nb + lr] = uv[i];
+          if (r < len) uw[((int64_t)(t0 + r) * H_v + h) * d_v + col0 + lr] = uv[i];
         }
       }
-    }
-    const float el = op.el;
-    load_uf(op, nx);
-    __syncthreads();
-    // 4. S <- e^{G_last} S + K^T U'' for this wave's rows; U', the factors and
-    //    K^T of the next chunk stream in behind
-    bf16x8 bh[NB][2], bl[NB][2];
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
+      const float el = op.el;
+      load_uf(op, cn);
+      __syncthreads();  // 2
+      // 3. S <- e^{G_last} S + K^T U'' for this wave's rows
+      bf16x8 bh[2], bl[2];
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
-        bh[nb][st] = as_bf(cat(u2x[nb][2 * st][0][lane], u2x[nb][2 * st + 1][0][lane]));
-        bl[nb][st] = as_bf(cat(u2x[nb][2 * st][1][lane], u2x[nb][2 * st + 1][1][lane]));
+        bh[st] = as_bf(u2x[st][0][lane]);
+        bl[st] = as_bf(u2x[st][1][lane]);
       }
+      const u32x4 *K4 = kp(cn);
+      f32x4 ah[2], al[2];  // K^T U''_hi and K^T U''_lo: four independent chains
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        S[mt][nb] *= el;
+      for (int mt = 0; mt < 2; ++mt) {
+        ah[mt] = al[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int st = 0; st < 2; ++st) {
-          S[mt][nb] = mfma_bf16(as_bf(op.kt[mt][st]), bh[nb][st], S[mt][nb]);
-          S[mt][nb] = mfma_bf16(as_bf(op.kt[mt][st]), bl[nb][st], S[mt][nb]);
+          ah[mt] = mfma_bf16(as_bf(op.kt[mt][st]), bh[st], ah[mt]);
+          al[mt] = mfma_bf16(as_bf(op.kt[mt][st]), bl[st], al[mt]);
+          op.kt[mt][st] = K4[(mt * 2 + st) * 64];
         }
       }
-      load_kt(op, nx, mt);
-    }
-    __builtin_amdgcn_sched_group_barrier(kDSR, 8 * NB, 0);
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      __builtin_amdgcn_sched_group_barrier(kMFMA, NB, 0);
-      if (k == 3 || k == 7) __builtin_amdgcn_sched_group_barrier(kVMR, 2, 0);
-    }
-    //    O = e^G q-norm (Q S) + P U for token tile w; P of the next chunk behind it
+      for (int mt = 0; mt < 2; ++mt) S[mt] = S[mt] * el + (ah[mt] + al[mt]);
+      __builtin_amdgcn_sched_group_barrier(kDSR, 4, 0);
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
+      for (int k = 0; k < 4; ++k) {
+        __builtin_amdgcn_sched_group_barrier(kMFMA, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(kVMR, 1, 0);
+      }
+    };
+
+    if (c_begin < c_end) {
+      StateOps op;
+      {
+        const u32x4 *W4 = wp(c_begin), *K4 = kp(c_begin);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          op.w[s][0] = W4[(s * 2 + 0) * 64];
+          op.w[s][1] = W4[(s * 2 + 1) * 64];
+        }
+        load_uf(op, c_begin);
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+          for (int st = 0; st < 2; ++st) op.kt[mt][st] = K4[(mt * 2 + st) * 64];
+      }
+      // The first chunk is peeled, so that the loop is entered with the same
+      // loads in flight as on its back edge (the compiler's wait counts are then
+      // exact).  Past the last chunk the loads repeat it and go unused.
+      chunk(op, c_begin, min(c_begin + 1, c_end - 1));
+      for (int c = c_begin + 1; c < c_end; ++c) chunk(op, c, min(c + 1, c_end - 1));
+    }
+    if (fin) {
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) fin[(sbase + 32 * w + 16 * mt + 4 * lg + i) * d_v + col0 + lr] = S[mt][i];
+    }
+  } else {
+    // ------------------------------ output waves -----------------------------
+    auto qp = [&](int c) { return reinterpret_cast<const u32x4 *>(qf + (jslot + c) * kWyQBytes) + w * 4 * 64 + lane; };
+    auto pp = [&](int c) { return reinterpret_cast<const u32x4 *>(pf + (hslot + c) * kWyPBytes) + w * 2 * 2 * 64 + lane; };
+    auto fq_of = [&](int c) { return *reinterpret_cast<const f32x4 *>(fac + (hslot + c) * kWyFac + 16 * w + 4 * lg); };
+    auto load_p = [&](OutOps &op, int c) {
+      const u32x4 *P4 = pp(c);
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+        if (st <= (w >> 1))  // P is lower triangular: token tiles 0, 1 use step 0 only
+#pragma unroll
+          for (int pl = 0; pl < 2; ++pl) op.p[st][pl] = P4[(st * 2 + pl) * 64];
+    };
+
+    auto chunk = [&](OutOps &op, int c, int cn) {
+      const int t0 = s_begin + (c - c_begin) * C;
+      const int len = min(C, s_end - t0);
+      __syncthreads();  // 1
+      __syncthreads();  // 2
+      // Q S for token tile w, from the S published for this chunk
+      f32x4 aq = {0.f, 0.f, 0.f, 0.f}, aq2 = aq;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const bf16x8 sh = as_bf(sx[c & 1][s][0][lane]), sl = as_bf(sx[c & 1][s][1][lane]);
+        aq = mfma_bf16(as_bf(op.q[s]), sh, aq);
+        aq2 = mfma_bf16(as_bf(op.q[s]), sl, aq2);
+      }
+      aq = (aq + aq2) * op.fq;
+      // O = e^G q-norm (Q S) + P U for token tile w
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
-        if (st <= (w >> 1)) {  // P is lower triangular
-          const bf16x8 bh2 = as_bf(cat(ux[nb][2 * st][0][lane], ux[nb][2 * st + 1][0][lane]));
-          const bf16x8 bl2 = as_bf(cat(ux[nb][2 * st][1][lane], ux[nb][2 * st + 1][1][lane]));
-          aq[nb] = mfma_bf16(as_bf(op.p[st][0]), bh2, aq[nb]);
-          aq[nb] = mfma_bf16(as_bf(op.p[st][0]), bl2, aq[nb]);
-          aq[nb] = mfma_bf16(as_bf(op.p[st][1]), bh2, aq[nb]);
+        if (st <= (w >> 1)) {
+          const bf16x8 bh = as_bf(ux[c & 1][st][0][lane]), bl = as_bf(ux[c & 1][st][1][lane]);
+          aq = mfma_bf16(as_bf(op.p[st][0]), bh, aq);
+          aq = mfma_bf16(as_bf(op.p[st][0]), bl, aq);
+          aq = mfma_bf16(as_bf(op.p[st][1]), bh, aq);
         }
       }
-    }
-    load_p(op, nx);
-    if (o) {
-      // The O tile goes through LDS so that each lane stores 4 consecutive
-      // columns of one row: lane l takes row l%16 and columns 4(l/16) + 16 m.
+      // the next chunk's operands
+      {
+        const u32x4 *Q4 = qp(cn);
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
+        for (int s = 0; s < 4; ++s) op.q[s] = Q4[s * 64];
+        op.fq = fq_of(cn);
+        load_p(op, cn);
+      }
+      if (o) {
+        // through LDS, so that each lane stores 4 consecutive columns of one
+        // row: lane l takes row l%16 and columns 4(l/16) ..
 #pragma unroll
-        for (int i = 0; i < 4; ++i) ot[w][(4 * lg + i) * LDO + 16 * nb + lr] = aq[nb][i];
-      __builtin_amdgcn_wave_barrier();
-      const int r = 16 * w + lr;  // row of the chunk
-      if (r < len) {
-        const f32x4 *src = reinterpret_cast<const f32x4 *>(&ot[w][lr * LDO + 4 * lg]);
-        const int64_t ob = ((int64_t)(t0 + r) * H_v + h) * d_v + col0 + 4 * lg;
-#pragma unroll
-        for (int m = 0; m < NB; ++m) {
-          const f32x4 x = src[4 * m];
+        for (int i = 0; i < 4; ++i) ot[w][(4 * lg + i) * LDO + lr] = aq[i];
+        __builtin_amdgcn_wave_barrier();
+        const int r = 16 * w + lr;
+        if (r < len) {
+          const f32x4 x = *reinterpret_cast<const f32x4 *>(&ot[w][lr * LDO + 4 * lg]);
+          const int64_t ob = ((int64_t)(t0 + r) * H_v + h) * d_v + col0 + 4 * lg;
           if constexpr (OBF16) {
-            *reinterpret_cast<u32x2 *>(static_cast<uint16_t *>(o) + ob + 16 * m) =
-                u32x2{pk_bf16(x[0], x[1]), pk_bf16(x[2], x[3])};
+            *reinterpret_cast<u32x2 *>(static_cast<uint16_t *>(o) + ob) = u32x2{pk_bf16(x[0], x[1]), pk_bf16(x[2], x[3])};
           } else {
-            *reinterpret_cast<f32x4 *>(static_cast<float *>(o) + ob + 16 * m) = x;
+            *reinterpret_cast<f32x4 *>(static_cast<float *>(o) + ob) = x;
           }
         }
       }
-    }
-  };
+    };
 
-  // One register set.  The first chunk is peeled, so that the loop is entered
-  // with the same memory operations in flight as on its back edge (the
-  // compiler's wait counts are then exact).  Past the last chunk the loads
-  // repeat the last chunk (always valid memory) and go unused.
-  if (c_begin < c_end) {
-    ChainOps<NB> op;
-    {
-      const Src a = src(c_begin);
+    if (c_begin < c_end) {
+      OutOps op;
+      {
+        const u32x4 *Q4 = qp(c_begin);
 #pragma unroll
-      for (int s4 = 0; s4 < 4; ++s4) load_wq(op, a, s4);
-      load_uf(op, a);
-      load_kt(op, a, 0);
-      load_kt(op, a, 1);
-      load_p(op, a);
+        for (int s = 0; s < 4; ++s) op.q[s] = Q4[s * 64];
+        op.fq = fq_of(c_begin);
+        load_p(op, c_begin);
+      }
+      chunk(op, c_begin, min(c_begin + 1, c_end - 1));
+      for (int c = c_begin + 1; c < c_end; ++c) chunk(op, c, min(c + 1, c_end - 1));
     }
-    chunk(op, c_begin, min(c_begin + 1, c_end - 1));
-    for (int c = c_begin + 1; c < c_end; ++c) chunk(op, c, min(c + 1, c_end - 1));
-  }
-
-  if (fin) {
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          fin[(sbase + 32 * w + 16 * mt + 4 * lg + i) * d_v + col0 + 16 * nb + lr] = S[mt][nb][i];
   }
 }
 
-template <int NB, bool STATES, bool OBF16>
+template <bool STATES, bool OBF16>
 hipError_t run_wy(const Problem &p, const ChunkArgs &a, hipStream_t st) {
   const Workspace &w = a.ws;
   mark_event(a, 0, st);
@@ -686,10 +699,10 @@ hipError_t run_wy(const Problem &p, const ChunkArgs &a, hipStream_t st) {
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   mark_event(a, 2, st);
-  const int units = p.N * p.H_v * (p.d_v / (16 * NB));
+  const int units = p.N * p.H_v * (p.d_v / 16);
   if (units > 0) {
     const int grid = (units + 7) / 8 * 8;
-    hipLaunchKernelGGL((wy_chain_kernel<NB, STATES, OBF16>), dim3(grid), dim3(256), 0, st, q, a.s0, w.status,
+    hipLaunchKernelGGL((wy_chain_kernel<STATES, OBF16>), dim3(grid), dim3(512), 0, st, a.s0, w.status,
                        w.seq_start, w.chunk_first, w.wf, w.pf, w.uf, w.fac, w.ktf, w.qf, a.o, a.final_state, w.u,
                        w.sc, p.N, p.H_qk, p.H_v, p.d_v, p.max_chunks, units, grid);
     if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -707,8 +720,8 @@ hipError_t run_wy(const Problem &p, const ChunkArgs &a, hipStream_t st) {
 hipError_t launch_wy_path(const Problem &p, const ChunkArgs &a, bool states, hipStream_t st) {
   if (p.d_k != DK || p.C != C || p.d_v % 32 != 0 || p.d_v > 128) return hipErrorInvalidValue;
   const bool ob = p.o_dtype == GDN_BF16;
-  if (states) return ob ? run_wy<1, true, true>(p, a, st) : run_wy<1, true, false>(p, a, st);
-  return ob ? run_wy<1, false, true>(p, a, st) : run_wy<1, false, false>(p, a, st);
+  if (states) return ob ? run_wy<true, true>(p, a, st) : run_wy<true, false>(p, a, st);
+  return ob ? run_wy<false, true>(p, a, st) : run_wy<false, false>(p, a, st);
 }
 
 }  // namespace gdn
