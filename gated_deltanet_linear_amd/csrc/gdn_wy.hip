@@ -55,11 +55,20 @@ namespace {
 
 constexpr int DK = 128, C = 64;
 constexpr int LDQ = DK + 8;  // q, k rows (bf16)
-constexpr int LDT = C + 8;   // K^T, V^T, T', T'' rows (bf16)
+constexpr int LDT = C + 2;   // K^T, V^T rows (bf16): an odd number of words spreads the
+                             // transposing 2-byte stores over the LDS banks
 constexpr int LDF = C + 4;   // fp32 C x C
 constexpr float kFloor = -1.0e4f;
 
 __device__ __forceinline__ bf16x8 ld8(const uint16_t *p) { return *reinterpret_cast<const bf16x8 *>(p); }
+// 8 bf16 from a 4-byte aligned LDS address.
+__device__ __forceinline__ bf16x8 ld8w(const uint16_t *p) {
+  const uint32_t *q = reinterpret_cast<const uint32_t *>(p);
+  return __builtin_bit_cast(bf16x8, u32x4{q[0], q[1], q[2], q[3]});
+}
+// e^x on the hardware exponential (v_exp_f32 of x log2 e): relative error a few
+// ulp for the decay arguments met here (|x| below a few hundred).
+__device__ __forceinline__ float fexp(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
 __device__ __forceinline__ bf16x8 as_bf(const u32x4 &x) { return __builtin_bit_cast(bf16x8, x); }
 
 // Two fp32 values -> one packed bf16 pair (v_cvt_pk_bf16_f32, round to nearest
@@ -154,7 +163,7 @@ __global__ __launch_bounds__(256) void wy_prep_kernel(
     const double gv = lane < len ? (double)fmaxf(graw, kFloor) : 0.0;
     const double gm = wave_inclusive_scan(gv, lane);
     sm.gam[lane] = gm;
-    sm.eg[lane] = expf((float)gm);
+    sm.eg[lane] = fexp((float)gm);
     sm.beta[lane] = lane < len ? braw : 0.f;
   }
   __syncthreads();
@@ -223,7 +232,7 @@ __global__ __launch_bounds__(256) void wy_prep_kernel(
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int ci = 16 * m + 4 * lg + e;
-          pv[e] = ci <= r ? sm.rq[r] * sm.rk[ci] * expf((float)(sm.gam[r] - sm.gam[ci])) * acc[m][e] : 0.f;
+          pv[e] = ci <= r ? sm.rq[r] * sm.rk[ci] * fexp((float)(sm.gam[r] - sm.gam[ci])) * acc[m][e] : 0.f;
         }
         u32x2 hi, lo;
         split4(pv, hi, lo);
@@ -242,7 +251,7 @@ __global__ __launch_bounds__(256) void wy_prep_kernel(
         for (int e = 0; e < 4; ++e) {
           const int rr = 16 * mi + 4 * lg + e, ci = 16 * ni + lr;
           A[rr * LDF + ci] = ci < rr ? sm.beta[rr] * sm.rk[rr] * sm.rk[ci] *
-                                           expf((float)(sm.gam[rr] - sm.gam[ci])) * acc[m][e]
+                                           fexp((float)(sm.gam[rr] - sm.gam[ci])) * acc[m][e]
                                      : 0.f;
         }
       }
@@ -253,8 +262,8 @@ __global__ __launch_bounds__(256) void wy_prep_kernel(
     float *F = fac + slot * kWyFac;
     const double gl = sm.gam[len - 1];
     F[tid] = sm.eg[tid] * sm.rq[tid];
-    F[C + tid] = tid < len ? expf((float)(gl - sm.gam[tid])) * sm.rk[tid] : 0.f;
-    if (tid == 0) F[2 * C] = expf((float)gl);
+    F[C + tid] = tid < len ? fexp((float)(gl - sm.gam[tid])) * sm.rk[tid] : 0.f;
+    if (tid == 0) F[2 * C] = fexp((float)gl);
   }
   __syncthreads();
 
@@ -352,7 +361,7 @@ __global__ __launch_bounds__(256) void wy_prep_kernel(
       for (int st = 0; st < 2; ++st) {
         if (st <= (w >> 1)) {  // T' is lower triangular
           const int ko = 32 * st + 8 * lg;
-          const bf16x8 a0 = ld8(kt + (32 * s + lr) * LDT + ko), a1 = ld8(kt + (32 * s + 16 + lr) * LDT + ko);
+          const bf16x8 a0 = ld8w(kt + (32 * s + lr) * LDT + ko), a1 = ld8w(kt + (32 * s + 16 + lr) * LDT + ko);
           acc0 = mfma_bf16(a0, as_bf(t1h[st]), acc0);
           acc0 = mfma_bf16(a0, as_bf(t1l[st]), acc0);
           acc1 = mfma_bf16(a1, as_bf(t1h[st]), acc1);
@@ -374,7 +383,7 @@ __global__ __launch_bounds__(256) void wy_prep_kernel(
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
         if (st <= (w >> 1)) {
-          const bf16x8 b = ld8(vt + (16 * ct + lr) * LDT + 32 * st + 8 * lg);
+          const bf16x8 b = ld8w(vt + (16 * ct + lr) * LDT + 32 * st + 8 * lg);
           a = mfma_bf16(as_bf(t2h[st]), b, a);
           a = mfma_bf16(as_bf(t2l[st]), b, a);
         }
@@ -389,7 +398,8 @@ __global__ __launch_bounds__(256) void wy_prep_kernel(
     for (int it = tid; it < 16 * 64; it += 256) {
       const int ln = it & 63, ms = it >> 6, mt = ms >> 1, st = ms & 1;
       const uint16_t *row = kt + (16 * mt + (ln & 15)) * LDT + 32 * st + 4 * (ln >> 4);
-      K4[it] = cat(*reinterpret_cast<const u32x2 *>(row), *reinterpret_cast<const u32x2 *>(row + 16));
+      const uint32_t *r32 = reinterpret_cast<const uint32_t *>(row);
+      K4[it] = u32x4{r32[0], r32[1], r32[8], r32[9]};
     }
   }
 }
