@@ -734,15 +734,18 @@ __global__ __launch_bounds__(512) void carry_kernel(
 // ---------------------------------------------------------------------------
 // stream: the state after every token, S <- e^{g_t} S + k_t u_t^T, from the
 // chunk-start state and the write vectors of the carry phase.  Workgroup =
-// (chunk, value head, block of RB rows of S); thread = 4 columns of one row.
+// (chunk, value head, block of RS * SRPT rows of S); a thread owns 4 columns of
+// SRPT rows (rows rl + RS i), so that each wave store covers consecutive rows,
+// and streams them out token by token with non-temporal 16-byte stores.
 // ---------------------------------------------------------------------------
-template <typename TIn, int C>
+template <typename TIn, int C, int SRPT>
 __global__ __launch_bounds__(256) void stream_kernel(
     const TIn *__restrict__ k, const float *__restrict__ g, const float *__restrict__ uw,
     const float *__restrict__ scw, const int32_t *__restrict__ status,
     const int32_t *__restrict__ seq_start, const int32_t *__restrict__ chunk_first,
     float *__restrict__ states, int N, int H_qk, int H_v, int d_k, int d_v, int l2norm) {
-  extern __shared__ float ssm[];  // u [C][d_v], kk [C][RB], alpha [C]
+  extern __shared__ float ssm[];  // u [C][d_v], kk [C][RS][SRPT], alpha [C]
+  static_assert(SRPT % 4 == 0 || SRPT == 1, "k factors are read 4 at a time");
   if (*status) return;
   const int c = blockIdx.x;
   if (c >= chunk_first[N]) return;
@@ -750,10 +753,10 @@ __global__ __launch_bounds__(256) void stream_kernel(
   const int t0 = seq_start[n] + (c - chunk_first[n]) * C;
   const int len = min(C, seq_start[n + 1] - t0);
   const int h = blockIdx.y, j = h / (H_v / H_qk);
-  const int CGn = d_v / 4, RB = 256 / CGn;
-  const int row0 = blockIdx.z * RB;
+  const int CGn = d_v / 4, RS = 256 / CGn, SR = RS * SRPT;
+  const int row0 = blockIdx.z * SR;
   const int tid = threadIdx.x, cg = tid % CGn, rl = tid / CGn;
-  float *us = ssm, *kk = ssm + C * d_v, *al = kk + C * RB;
+  float *us = ssm, *kk = ssm + C * d_v, *al = kk + C * SR;
   const int64_t slot = (int64_t)c * H_v + h;
 
   for (int x = tid; x < len * CGn; x += 256) {
@@ -773,20 +776,45 @@ __global__ __launch_bounds__(256) void stream_kernel(
       }
       rk = 1.0f / sqrtf(ss + 1e-6f);
     }
-    for (int i = 0; i < RB; ++i) kk[r * RB + i] = (row0 + i < d_k) ? Elem<TIn>::get(kr, row0 + i) * rk : 0.f;
+    for (int x = 0; x < SR; ++x) {  // kk[r][rr][i]: factor of row row0 + rr + RS i
+      const int rr = x / SRPT, i = x % SRPT, row = row0 + rr + RS * i;
+      kk[r * SR + x] = (row < d_k) ? Elem<TIn>::get(kr, row) * rk : 0.f;
+    }
     al[r] = expf(g[(int64_t)(t0 + r) * H_v + h]);
   }
   __syncthreads();
-  const int row = row0 + rl;
-  if (rl >= RB || row >= d_k) return;  // tail threads when 256 % (d_v / 4) != 0
-  f32x4 Sv = *reinterpret_cast<const f32x4 *>(scw + (slot * d_k + row) * d_v + 4 * cg);
-  const int64_t sstride = (int64_t)H_v * d_k * d_v;
-  f32x4 *dst = reinterpret_cast<f32x4 *>(states + ((int64_t)t0 * H_v + h) * d_k * d_v + (int64_t)row * d_v + 4 * cg);
+  if (rl >= RS) return;  // tail threads when 256 % (d_v / 4) != 0
+  f32x4 Sv[SRPT];
+  const int64_t sstride = (int64_t)H_v * d_k * d_v;  // one token
+  const int64_t rstride = (int64_t)RS * d_v;          // from row i to row i + 1 of this thread
+  float *dst = states + ((int64_t)t0 * H_v + h) * d_k * d_v + (int64_t)(row0 + rl) * d_v + 4 * cg;
+#pragma unroll
+  for (int i = 0; i < SRPT; ++i) {
+    const int row = min(row0 + rl + RS * i, d_k - 1);  // rows past d_k: computed, not stored
+    Sv[i] = *reinterpret_cast<const f32x4 *>(scw + (slot * d_k + row) * d_v + 4 * cg);
+  }
+  const bool full = row0 + SR <= d_k;
   for (int r = 0; r < len; ++r) {
     const f32x4 uv = *reinterpret_cast<const f32x4 *>(us + r * d_v + 4 * cg);
-    Sv = al[r] * Sv + kk[r * RB + rl] * uv;
-    __builtin_nontemporal_store(Sv, dst);
-    dst += sstride / 4;
+    const float a = al[r];
+    float kf[SRPT];
+    if constexpr (SRPT == 1) {
+      kf[0] = kk[r * SR + rl];
+    } else {
+#pragma unroll
+      for (int i4 = 0; i4 < SRPT; i4 += 4) {
+        const f32x4 k4 = *reinterpret_cast<const f32x4 *>(kk + r * SR + rl * SRPT + i4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) kf[i4 + e] = k4[e];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < SRPT; ++i) {
+      Sv[i] = a * Sv[i] + kf[i] * uv;
+      if (full || row0 + rl + RS * i < d_k)
+        __builtin_nontemporal_store(Sv[i], reinterpret_cast<f32x4 *>(dst + i * rstride));
+    }
+    dst += sstride;
   }
 }
 
@@ -800,14 +828,14 @@ hipError_t launch_plan(const Problem &p, const ChunkArgs &a, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <typename TIn, int C>
+template <typename TIn, int C, int SRPT>
 static hipError_t stream_t(const Problem &p, const ChunkArgs &a, hipStream_t st) {
   const Workspace &w = a.ws;
-  const int CGn = p.d_v / 4, RB = 256 / CGn;
-  const int zb = ceil_div(p.d_k, RB);
+  const int CGn = p.d_v / 4, SR = (256 / CGn) * SRPT;
+  const int zb = ceil_div(p.d_k, SR);
   if (p.max_chunks > 0 && p.H_v > 0 && zb > 0) {
-    const size_t shm = sizeof(float) * ((size_t)C * p.d_v + (size_t)C * RB + C);
-    hipLaunchKernelGGL((stream_kernel<TIn, C>), dim3(p.max_chunks, p.H_v, zb), dim3(256), shm, st,
+    const size_t shm = sizeof(float) * ((size_t)C * p.d_v + (size_t)C * SR + C);
+    hipLaunchKernelGGL((stream_kernel<TIn, C, SRPT>), dim3(p.max_chunks, p.H_v, zb), dim3(256), shm, st,
                        static_cast<const TIn *>(a.k), a.g, w.u, w.sc, w.status, w.seq_start, w.chunk_first,
                        a.states, p.N, p.H_qk, p.H_v, p.d_k, p.d_v, p.l2norm ? 1 : 0);
     return hipGetLastError();
@@ -815,9 +843,18 @@ static hipError_t stream_t(const Problem &p, const ChunkArgs &a, hipStream_t st)
   return hipSuccess;
 }
 
+// Rows per thread: as many as keep the row block within d_k (16, 4 or 1).
+template <typename TIn, int C>
+static hipError_t stream_rows(const Problem &p, const ChunkArgs &a, hipStream_t st) {
+  const int RS = 256 / (p.d_v / 4);
+  if (RS * 16 <= p.d_k) return stream_t<TIn, C, 16>(p, a, st);
+  if (RS * 4 <= p.d_k) return stream_t<TIn, C, 4>(p, a, st);
+  return stream_t<TIn, C, 1>(p, a, st);
+}
+
 hipError_t launch_states_stream(const Problem &p, const ChunkArgs &a, hipStream_t st) {
-  if (p.dtype == GDN_BF16 && p.C == 64) return stream_t<uint16_t, 64>(p, a, st);
-  if (p.dtype == GDN_F32 && p.C == 16) return stream_t<float, 16>(p, a, st);
+  if (p.dtype == GDN_BF16 && p.C == 64) return stream_rows<uint16_t, 64>(p, a, st);
+  if (p.dtype == GDN_F32 && p.C == 16) return stream_rows<float, 16>(p, a, st);
   return hipErrorInvalidValue;
 }
 

@@ -11,10 +11,11 @@
 //   o = a r + (k . q) d             = S_new^T q, read after the write
 //
 // The step is a pure HBM stream (0.74 FLOP per byte): one workgroup per
-// (b, h); each thread keeps a 4-column x (d_k / row groups)-row strip of S in
-// registers between the read and the write, so S crosses HBM exactly twice.
-// Loads and stores are 16 bytes per lane, and each wave instruction touches two
-// whole 512-byte rows of S.
+// (b, h) of up to 1024 threads; each thread keeps a 4-column x (d_k / row
+// groups)-row strip of S in registers between the read and the write, so S
+// crosses HBM exactly twice.  Loads and stores are 16 bytes per lane and
+// non-temporal (the state is not reused before the next step), and each wave
+// instruction touches two whole 512-byte rows of S.
 #include "gdn_device.hpp"
 #include "gdn_internal.hpp"
 #include "gdn.h"
@@ -23,7 +24,7 @@ namespace gdn {
 
 template <int DK, int DV> struct StepCfg {
   static constexpr int CG = DV / 4;                                   // float4 column groups
-  static constexpr int NT = (DK * DV / 4 < 256) ? DK * DV / 4 : 256;  // threads
+  static constexpr int NT = (DK * DV / 4 < 1024) ? DK * DV / 4 : 1024;  // threads
   static constexpr int RG = NT / CG;                                  // row groups
   static constexpr int RPT = DK / RG;                                 // rows per thread
   static constexpr int NW = (NT + 63) / 64;                           // waves
@@ -54,7 +55,7 @@ __global__ __launch_bounds__((StepCfg<DK, DV>::NT)) void step_kernel(
   f32x4 S[RPT];
 #pragma unroll
   for (int s = 0; s < RPT; ++s)
-    S[s] = *reinterpret_cast<const f32x4 *>(Sp + (int64_t)(rg + RG * s) * DV + 4 * cg);
+    S[s] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(Sp + (int64_t)(rg + RG * s) * DV + 4 * cg));
 
   const int64_t qk_off = ((int64_t)b * H_qk + j) * DK;
   for (int i = tid; i < DK; i += Cfg::NT) {
@@ -136,7 +137,7 @@ __global__ __launch_bounds__((StepCfg<DK, DV>::NT)) void step_kernel(
   for (int s = 0; s < RPT; ++s) {
     const int row = rg + RG * s;
     const float kk = ks[row] * rk;
-    *reinterpret_cast<f32x4 *>(Sp + (int64_t)row * DV + 4 * cg) = alpha * S[s] + kk * d;
+    __builtin_nontemporal_store(alpha * S[s] + kk * d, reinterpret_cast<f32x4 *>(Sp + (int64_t)row * DV + 4 * cg));
   }
   if (rg == 0) {
     const f32x4 out = alpha * r + kq * d;
