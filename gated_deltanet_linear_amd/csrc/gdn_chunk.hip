@@ -1,4 +1,7 @@
-// The chunked paths of libgdn: gdn_chunk_fwd and gdn_states_fwd.
+// The chunked paths of libgdn: the pieces every input type shares (the plan
+// kernel, the per-token states stream, the launchers and the workspace
+// layout) and the fp32 path (d_k = 16, chunk 16); bf16 inputs take the path in
+// gdn_wy.hip.
 //
 // What is computed is the gated delta rule of the pages (Qwen3.5 text
 // encyclopedia page, note "The DeltaNet mixer"; value table of
@@ -12,27 +15,24 @@
 //   O      = diag(e^G) Q S + P U,  P[r,i] = e^{G_r-G_i} (q_r . k_i), i <= r
 //   S     <- e^{G_last} S + K^T diag(e^{G_last - G}) U
 //
-// Launch sequence on the caller's stream:
+// fp32 launch sequence on the caller's stream:
 //   plan   (1 workgroup)  sequence starts and chunk numbering from cu_seqlens
 //   prep   (chunk, qk head)  K K^T and Q K^T on MFMA, the fp32 triangular solve,
 //                           T diag(beta), P and the decay vectors -> workspace.
 //                           Both value heads of a query/key head share K K^T, Q K^T.
-//   carry  (sequence, value head, 32-column block of S)  walks the chunks of
-//                           one sequence in order with its S block in registers:
-//                           [Q;K] S, T diag(beta) X, P U and K^T U on MFMA.
+//   carry  (sequence, value head, column block of S)  walks the chunks of one
+//                           sequence in order with its S block in registers:
+//                           [Q;K] S, T diag(beta) X, P U and K^T U on fp32 MFMA.
 //                           The delta rule acts on each column of S on its own,
 //                           so column blocks are independent chains.
 //   stream (states path only)  S after every token from the chunk-start
 //                           state and the write vectors: S <- e^g S + k u^T,
-//                           one non-temporal 16-byte store per element group.
+//                           non-temporal 16-byte stores.
 //
-// Precision: S, all products' accumulators and the solve are fp32.  On the
-// bf16 path every operand that is a computed fp32 value (S, T diag(beta), X, P,
-// U) enters MFMA as a bf16 hi/lo pair (hi*hi + hi*lo + lo*hi); q, k, v are exact
-// bf16 inputs and enter once.  Decays are summed in fp64 and every factor
-// e^{G_r - G_i} is formed from a difference with r >= i, so it never overflows;
-// g is clamped to -1e4, which keeps -inf (a reset) finite and still gives
-// exp() == 0 for every factor that spans it.
+// Decays are summed in fp64 and every factor e^{G_r - G_i} is formed from a
+// difference with r >= i, so it never overflows; g is clamped to -1e4, which
+// keeps -inf (a reset) finite and still gives exp() == 0 for every factor that
+// spans it.
 #include <type_traits>
 
 #include "gdn_device.hpp"
