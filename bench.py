@@ -112,12 +112,18 @@ def prepare_chunk(lib, b, d, states=False):
 
 def timed_chunk_calls(lib, calls, steps, warmup, n_kernels):
     """Warm up, then time `steps` calls (rotating over `calls`) with the host clock between
-    synchronisations, and each kernel of every timed call with HIP events recorded on the
-    launch stream by the library's timing hook.  Returns (ms per call, [ms per kernel])."""
+    synchronisations and no instrumentation; then time each kernel over another `steps`
+    calls with HIP events that the library's timing hook records on the launch stream
+    between its kernels.  Returns (ms per call, [ms per kernel])."""
     import torch
     for i in range(warmup):
         calls[i % len(calls)]()
     torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        calls[i % len(calls)]()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_kernels + 1)] for _ in range(steps)]
     for row in evs:          # torch creates an event's handle at its first record
         for e in row:
@@ -126,12 +132,10 @@ def timed_chunk_calls(lib, calls, steps, warmup, n_kernels):
     arrays = [(ctypes.c_void_p * (n_kernels + 1))(*[ctypes.c_void_p(e.cuda_event) for e in row])
               for row in evs]
     assert all(e.cuda_event for row in evs for e in row)
-    t0 = time.perf_counter()
     for i in range(steps):
         lib.gdn_set_timing_events(arrays[i], n_kernels + 1)
         calls[i % len(calls)]()
     torch.cuda.synchronize()
-    t1 = time.perf_counter()
     lib.gdn_set_timing_events(None, 0)
     per_kernel = [sum(row[j].elapsed_time(row[j + 1]) for row in evs) / steps for j in range(n_kernels)]
     return (t1 - t0) * 1e3 / steps, per_kernel

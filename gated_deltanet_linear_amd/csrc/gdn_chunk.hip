@@ -741,17 +741,16 @@ __global__ __launch_bounds__(512) void carry_kernel(
 template <typename TIn, int C, int SRPT>
 __global__ __launch_bounds__(256) void stream_kernel(
     const TIn *__restrict__ k, const float *__restrict__ g, const float *__restrict__ uw,
-    const float *__restrict__ scw, const int32_t *__restrict__ status,
-    const int32_t *__restrict__ seq_start, const int32_t *__restrict__ chunk_first,
-    float *__restrict__ states, int N, int H_qk, int H_v, int d_k, int d_v, int l2norm) {
+    const float *__restrict__ scw, const Seqs sq, float *__restrict__ states, int H_qk, int H_v, int d_k,
+    int d_v, int l2norm) {
   extern __shared__ float ssm[];  // u [C][d_v], kk [C][RS][SRPT], alpha [C]
   static_assert(SRPT % 4 == 0 || SRPT == 1, "k factors are read 4 at a time");
-  if (*status) return;
+  if (sq.bad()) return;
   const int c = blockIdx.x;
-  if (c >= chunk_first[N]) return;
-  const int n = find_seq(chunk_first, N, c);
-  const int t0 = seq_start[n] + (c - chunk_first[n]) * C;
-  const int len = min(C, seq_start[n + 1] - t0);
+  if (c >= sq.chunks()) return;
+  const int n = sq.seq_of(c);
+  const int t0 = sq.start(n) + (c - sq.first(n)) * C;
+  const int len = min(C, sq.start(n + 1) - t0);
   const int h = blockIdx.y, j = h / (H_v / H_qk);
   const int CGn = d_v / 4, RS = 256 / CGn, SR = RS * SRPT;
   const int row0 = blockIdx.z * SR;
@@ -829,15 +828,15 @@ hipError_t launch_plan(const Problem &p, const ChunkArgs &a, hipStream_t st) {
 }
 
 template <typename TIn, int C, int SRPT>
-static hipError_t stream_t(const Problem &p, const ChunkArgs &a, hipStream_t st) {
+static hipError_t stream_t(const Problem &p, const ChunkArgs &a, const Seqs &sq, hipStream_t st) {
   const Workspace &w = a.ws;
   const int CGn = p.d_v / 4, SR = (256 / CGn) * SRPT;
   const int zb = ceil_div(p.d_k, SR);
   if (p.max_chunks > 0 && p.H_v > 0 && zb > 0) {
     const size_t shm = sizeof(float) * ((size_t)C * p.d_v + (size_t)C * SR + C);
     hipLaunchKernelGGL((stream_kernel<TIn, C, SRPT>), dim3(p.max_chunks, p.H_v, zb), dim3(256), shm, st,
-                       static_cast<const TIn *>(a.k), a.g, w.u, w.sc, w.status, w.seq_start, w.chunk_first,
-                       a.states, p.N, p.H_qk, p.H_v, p.d_k, p.d_v, p.l2norm ? 1 : 0);
+                       static_cast<const TIn *>(a.k), a.g, w.u, w.sc, sq, a.states, p.H_qk, p.H_v, p.d_k, p.d_v,
+                       p.l2norm ? 1 : 0);
     return hipGetLastError();
   }
   return hipSuccess;
@@ -845,16 +844,16 @@ static hipError_t stream_t(const Problem &p, const ChunkArgs &a, hipStream_t st)
 
 // Rows per thread: as many as keep the row block within d_k (16, 4 or 1).
 template <typename TIn, int C>
-static hipError_t stream_rows(const Problem &p, const ChunkArgs &a, hipStream_t st) {
+static hipError_t stream_rows(const Problem &p, const ChunkArgs &a, const Seqs &sq, hipStream_t st) {
   const int RS = 256 / (p.d_v / 4);
-  if (RS * 16 <= p.d_k) return stream_t<TIn, C, 16>(p, a, st);
-  if (RS * 4 <= p.d_k) return stream_t<TIn, C, 4>(p, a, st);
-  return stream_t<TIn, C, 1>(p, a, st);
+  if (RS * 16 <= p.d_k) return stream_t<TIn, C, 16>(p, a, sq, st);
+  if (RS * 4 <= p.d_k) return stream_t<TIn, C, 4>(p, a, sq, st);
+  return stream_t<TIn, C, 1>(p, a, sq, st);
 }
 
-hipError_t launch_states_stream(const Problem &p, const ChunkArgs &a, hipStream_t st) {
-  if (p.dtype == GDN_BF16 && p.C == 64) return stream_rows<uint16_t, 64>(p, a, st);
-  if (p.dtype == GDN_F32 && p.C == 16) return stream_rows<float, 16>(p, a, st);
+hipError_t launch_states_stream(const Problem &p, const ChunkArgs &a, const Seqs &sq, hipStream_t st) {
+  if (p.dtype == GDN_BF16 && p.C == 64) return stream_rows<uint16_t, 64>(p, a, sq, st);
+  if (p.dtype == GDN_F32 && p.C == 16) return stream_rows<float, 16>(p, a, sq, st);
   return hipErrorInvalidValue;
 }
 
@@ -887,7 +886,8 @@ static hipError_t run_t(const Problem &p, const ChunkArgs &a, hipStream_t st) {
   }
   mark_event(a, 3, st);
   if constexpr (STATES) {
-    if ((e = launch_states_stream(p, a, st)) != hipSuccess) return e;
+    const Seqs sq{w.status, w.seq_start, w.chunk_first, p.N, 0, 0};
+    if ((e = launch_states_stream(p, a, sq, st)) != hipSuccess) return e;
     mark_event(a, 4, st);
   }
   return hipSuccess;

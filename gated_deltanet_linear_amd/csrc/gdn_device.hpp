@@ -138,6 +138,21 @@ __device__ __forceinline__ int find_seq(const int32_t *chunk_first, int N, int c
   return lo;
 }
 
+// Where sequences and their chunks start.  Dense rows (no cu_seqlens, T > 0):
+// row n starts at token n T and its chunks at n ceil(T / C), no tables needed;
+// packed rows: the tables and the status word the plan kernel wrote.
+struct Seqs {
+  const int32_t *status, *seq_start, *chunk_first;
+  int N;    // sequences
+  int T;    // > 0: dense rows of T tokens; 0: use the tables
+  int cpr;  // chunks per dense row
+  __device__ __forceinline__ bool bad() const { return T == 0 && *status != 0; }
+  __device__ __forceinline__ int chunks() const { return T ? N * cpr : chunk_first[N]; }
+  __device__ __forceinline__ int seq_of(int c) const { return T ? c / cpr : find_seq(chunk_first, N, c); }
+  __device__ __forceinline__ int first(int n) const { return T ? n * cpr : chunk_first[n]; }
+  __device__ __forceinline__ int start(int n) const { return T ? n * T : seq_start[n]; }
+};
+
 // blockIdx -> logical work item, so that runs of consecutive logical items land
 // on one XCD (workgroups are dealt to the 8 XCDs round robin) and share its L2.
 // `grid` must be a multiple of 8.

@@ -78,7 +78,10 @@ hipError_t launch_chunk_path(const Problem &p, const ChunkArgs &a, bool states, 
 // Pieces shared by the chunked paths (gdn_chunk.hip): the plan kernel, the
 // per-token states stream, and the timing hook.
 hipError_t launch_plan(const Problem &p, const ChunkArgs &a, hipStream_t stream);
-hipError_t launch_states_stream(const Problem &p, const ChunkArgs &a, hipStream_t stream);
+// Dense rows (no cu_seqlens) need no plan: their geometry is n T and n ceil(T / C).
+inline bool dense_rows(const Problem &p) { return !p.packed && p.T > 0; }
+struct Seqs;
+hipError_t launch_states_stream(const Problem &p, const ChunkArgs &a, const Seqs &sq, hipStream_t stream);
 inline void mark_event(const ChunkArgs &a, int i, hipStream_t st) {
   if (a.events && i < a.n_events) (void)hipEventRecord(a.events[i], st);
 }

@@ -117,18 +117,17 @@ struct PrepSmem {
 
 __global__ __launch_bounds__(256) void wy_prep_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
-    const float *__restrict__ g, const float *__restrict__ beta, const int32_t *__restrict__ status,
-    const int32_t *__restrict__ seq_start, const int32_t *__restrict__ chunk_first,
+    const float *__restrict__ g, const float *__restrict__ beta, const Seqs seqs,
     unsigned char *__restrict__ wf, unsigned char *__restrict__ pf, float *__restrict__ uf,
-    float *__restrict__ fac, unsigned char *__restrict__ ktf, unsigned char *__restrict__ qf, int N, int H_qk,
+    float *__restrict__ fac, unsigned char *__restrict__ ktf, unsigned char *__restrict__ qf, int H_qk,
     int H_v, int d_v, int MC, float scale, int l2norm) {
   __shared__ PrepSmem sm;
-  if (*status) return;
+  if (seqs.bad()) return;
   const int c = blockIdx.x;
-  if (c >= chunk_first[N]) return;
-  const int n = find_seq(chunk_first, N, c);
-  const int t0 = seq_start[n] + (c - chunk_first[n]) * C;
-  const int len = min(C, seq_start[n + 1] - t0);
+  if (c >= seqs.chunks()) return;
+  const int n = seqs.seq_of(c);
+  const int t0 = seqs.start(n) + (c - seqs.first(n)) * C;
+  const int len = min(C, seqs.start(n + 1) - t0);
   const int h = blockIdx.y, R = H_v / H_qk, j = h / R;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -439,11 +438,10 @@ struct OutOps {
 
 template <bool STATES, bool OBF16>
 __global__ __launch_bounds__(512) void wy_chain_kernel(
-    const float *__restrict__ s0, const int32_t *__restrict__ status, const int32_t *__restrict__ seq_start,
-    const int32_t *__restrict__ chunk_first, const unsigned char *__restrict__ wf,
+    const float *__restrict__ s0, const Seqs sq, const unsigned char *__restrict__ wf,
     const unsigned char *__restrict__ pf, const float *__restrict__ uf, const float *__restrict__ fac,
     const unsigned char *__restrict__ ktf, const unsigned char *__restrict__ qf, void *__restrict__ o,
-    float *__restrict__ fin, float *__restrict__ uw, float *__restrict__ scw, int N, int H_qk, int H_v,
+    float *__restrict__ fin, float *__restrict__ uw, float *__restrict__ scw, int H_qk, int H_v,
     int d_v, int MC, int units, int grid) {
   // S and U as published by their owner wave, in the owner's lane order.
   // ux and u2x: the two token tiles of token step st side by side, so a reader
@@ -453,7 +451,7 @@ __global__ __launch_bounds__(512) void wy_chain_kernel(
   __shared__ u32x4 u2x[2][2][64];
   constexpr int LDO = 20;  // O tile rows, fp32 (the pad spreads rows over the banks)
   __shared__ float ot[4][16 * LDO];
-  if (*status) return;
+  if (sq.bad()) return;
   const int u = xcd_remap(blockIdx.x, grid);
   if (u >= units) return;
   const int NCT = d_v / 16;
@@ -465,8 +463,8 @@ __global__ __launch_bounds__(512) void wy_chain_kernel(
   const int lr = lane & 15, lg = lane >> 4;
   const int col0 = jb * 16;
   const int64_t sbase = (int64_t)(n * H_v + h) * DK;
-  const int c_begin = chunk_first[n], c_end = chunk_first[n + 1];
-  const int s_begin = seq_start[n], s_end = seq_start[n + 1];
+  const int c_begin = sq.first(n), c_end = sq.first(n + 1);
+  const int s_begin = sq.start(n), s_end = sq.start(n + 1);
   const int64_t hslot = (int64_t)h * MC, jslot = (int64_t)j * MC;
   constexpr int kMFMA = 0x008, kVMR = 0x020, kDSR = 0x100;  // scheduling-group classes
 
@@ -697,29 +695,31 @@ template <bool STATES, bool OBF16>
 hipError_t run_wy(const Problem &p, const ChunkArgs &a, hipStream_t st) {
   const Workspace &w = a.ws;
   mark_event(a, 0, st);
-  hipError_t e = launch_plan(p, a, st);
-  if (e != hipSuccess) return e;
+  hipError_t e;
+  const bool dense = dense_rows(p);
+  if (!dense && (e = launch_plan(p, a, st)) != hipSuccess) return e;
   mark_event(a, 1, st);
+  const Seqs sq{w.status, w.seq_start, w.chunk_first, p.N, dense ? p.T : 0, dense ? ceil_div(p.T, C) : 0};
   const uint16_t *q = static_cast<const uint16_t *>(a.q), *k = static_cast<const uint16_t *>(a.k),
                  *v = static_cast<const uint16_t *>(a.v);
   if (p.max_chunks > 0 && p.H_v > 0) {
     hipLaunchKernelGGL(wy_prep_kernel, dim3(p.max_chunks, p.H_v), dim3(256), 0, st, q, k, v, a.g, a.beta,
-                       w.status, w.seq_start, w.chunk_first, w.wf, w.pf, w.uf, w.fac, w.ktf, w.qf, p.N,
-                       p.H_qk, p.H_v, p.d_v, p.max_chunks, p.scale, p.l2norm ? 1 : 0);
+                       sq, w.wf, w.pf, w.uf, w.fac, w.ktf, w.qf, p.H_qk, p.H_v, p.d_v, p.max_chunks, p.scale,
+                       p.l2norm ? 1 : 0);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   mark_event(a, 2, st);
   const int units = p.N * p.H_v * (p.d_v / 16);
   if (units > 0) {
     const int grid = (units + 7) / 8 * 8;
-    hipLaunchKernelGGL((wy_chain_kernel<STATES, OBF16>), dim3(grid), dim3(512), 0, st, a.s0, w.status,
-                       w.seq_start, w.chunk_first, w.wf, w.pf, w.uf, w.fac, w.ktf, w.qf, a.o, a.final_state, w.u,
-                       w.sc, p.N, p.H_qk, p.H_v, p.d_v, p.max_chunks, units, grid);
+    hipLaunchKernelGGL((wy_chain_kernel<STATES, OBF16>), dim3(grid), dim3(512), 0, st, a.s0, sq, w.wf, w.pf,
+                       w.uf, w.fac, w.ktf, w.qf, a.o, a.final_state, w.u, w.sc, p.H_qk, p.H_v, p.d_v,
+                       p.max_chunks, units, grid);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   mark_event(a, 3, st);
   if constexpr (STATES) {
-    if ((e = launch_states_stream(p, a, st)) != hipSuccess) return e;
+    if ((e = launch_states_stream(p, a, sq, st)) != hipSuccess) return e;
     mark_event(a, 4, st);
   }
   return hipSuccess;
