@@ -504,7 +504,7 @@ __global__ __launch_bounds__(512) void carry_kernel(
     const unsigned char *__restrict__ tbw, const unsigned char *__restrict__ pmw,
     const float *__restrict__ egw, const float *__restrict__ ebw, void *__restrict__ o,
     float *__restrict__ fin, float *__restrict__ uw, float *__restrict__ scw, int N, int H_qk, int H_v,
-    int d_v, float scale, int l2norm, int units, int grid) {
+    int d_v, float scale, int l2norm, int groups) {
   using P = Pol<TIn>;
   using F = Fr<P::BF>;
   using SM = CarrySmem<TIn, DK, C, DVB>;
@@ -518,9 +518,9 @@ __global__ __launch_bounds__(512) void carry_kernel(
   __shared__ SM sm;
 
   if (*status) return;
-  const int u = xcd_remap(blockIdx.x, grid);
-  if (u >= units) return;
   const int NJB = d_v / DVB;
+  const int u = xcd_group_remap(blockIdx.x, NJB, groups);
+  if (u < 0) return;
   const int jb = u % NJB, h = (u / NJB) % H_v, n = u / (NJB * H_v);
   const int j = h / (H_v / H_qk);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -874,14 +874,13 @@ static hipError_t run_t(const Problem &p, const ChunkArgs &a, hipStream_t st) {
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   mark_event(a, 2, st);
-  const int units = p.N * p.H_v * (p.d_v / DVB);
-  if (units > 0) {
-    const int grid = (units + 7) / 8 * 8;
+  const int groups = p.N * p.H_v;
+  if (groups > 0 && p.d_v > 0) {
+    const int grid = xcd_group_grid(p.d_v / DVB, groups);
     hipLaunchKernelGGL((carry_kernel<TIn, DK, C, DVB, STATES, OBF16>), dim3(grid), dim3(512), 0, st, q, k, v,
                        a.s0, w.status, w.seq_start, w.chunk_first, reinterpret_cast<const unsigned char *>(w.tb),
                        reinterpret_cast<const unsigned char *>(w.pm), w.eg, w.eb, a.o,
-                       a.final_state, w.u, w.sc, p.N, p.H_qk, p.H_v, p.d_v, p.scale, p.l2norm ? 1 : 0, units,
-                       grid);
+                       a.final_state, w.u, w.sc, p.N, p.H_qk, p.H_v, p.d_v, p.scale, p.l2norm ? 1 : 0, groups);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   mark_event(a, 3, st);

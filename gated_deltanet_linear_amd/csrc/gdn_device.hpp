@@ -153,12 +153,19 @@ struct Seqs {
   __device__ __forceinline__ int start(int n) const { return T ? n * T : seq_start[n]; }
 };
 
-// blockIdx -> logical work item, so that runs of consecutive logical items land
-// on one XCD (workgroups are dealt to the 8 XCDs round robin) and share its L2.
-// `grid` must be a multiple of 8.
-__device__ __forceinline__ int xcd_remap(int bid, int grid) {
-  return (bid & 7) * (grid >> 3) + (bid >> 3);
+// blockIdx -> logical work item u = g * per + r, for work made of `groups`
+// groups of `per` items that share their operands (the column blocks of one
+// (sequence, head)).  Workgroups are dealt to the 8 XCDs round robin; this keeps
+// each group on one XCD, whose L2 then serves the group's shared reads, and
+// deals the groups themselves round robin, so that the first groups in u order
+// (the first sequences) spread over every XCD.  The grid is
+// 8 ceil(groups / 8) per blocks; padding blocks get -1.
+__device__ __forceinline__ int xcd_group_remap(int bid, int per, int groups) {
+  const int x = bid & 7, i = bid >> 3;
+  const int g = (i / per) * 8 + x;
+  return g < groups ? g * per + i % per : -1;
 }
+inline int xcd_group_grid(int per, int groups) { return (groups + 7) / 8 * 8 * per; }
 
 // Non-temporal 16-byte store (streamed output that is not read back soon).
 __device__ __forceinline__ void store_nt(float4 *p, const float4 &v) {

@@ -24,14 +24,13 @@
 // (sequence, value head, block of 16 NB value columns), and on the states path
 // the per-token stream (gdn_chunk.hip).
 //
-// Chain: 4 waves per block.  Wave w keeps rows [32w, 32w + 32) of the S block
-// in registers, and computes the token tile [16w, 16w + 16) of U and O.  Per
-// chunk it publishes its S rows in LDS (bf16 hi/lo), forms U = U' - W S and
-// Q S for its token tile, publishes U, then updates its S rows with K^T U and
-// finishes its O rows with P U: two barriers per chunk.  Every operand that
-// does not depend on S is loaded from the workspace straight into registers,
-// two chunks ahead, in the lane order of the MFMA that consumes it; nothing
-// but S and U passes through LDS.
+// Chain: 8 waves per block.  Waves 0-3 carry the state: wave w keeps rows
+// [32w, 32w + 32) of the S block in registers and forms U for the token tile
+// [16w, 16w + 16); waves 4-7 form O from the S and U that the state waves
+// publish in LDS (bf16 hi/lo): two barriers per chunk.  Every operand that does
+// not depend on S is loaded from the workspace straight into registers, one
+// chunk ahead, in the lane order of the MFMA that consumes it; nothing but S
+// and U passes through LDS.
 //
 // MFMA lane order (v_mfma_f32_16x16x32_bf16): lane l feeds row l%16 of A and
 // column l%16 of B, and 8 contraction indices given by the group l/16.  The
@@ -44,6 +43,7 @@
 //
 // Precision: as on the fp32 path, products of computed values (S, W, U, P)
 // enter MFMA as bf16 hi/lo pairs (hi*hi + hi*lo + lo*hi); q, k, v enter once.
+#include <atomic>
 #include <type_traits>
 
 #include "gdn_device.hpp"
@@ -404,11 +404,11 @@ __global__ __launch_bounds__(256) void wy_prep_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// chain: one (sequence, value head, 16-column block of S) per block of 8
-// waves.  Waves 0-3 carry the state: wave w keeps rows [32w, 32w + 32) of the
-// S block in registers and forms the write vectors U of token tile [16w, 16w +
-// 16).  Waves 4-7 produce the output: wave 4 + w computes O for token tile w
-// from the published S and U.  Per chunk c:
+// chain: one (sequence, value head, block of 16 NB columns of S) per block of
+// 8 waves.  Waves 0-3 carry the state: wave w keeps rows [32w, 32w + 32) of
+// the S block in registers and forms the write vectors U of token tile [16w,
+// 16w + 16).  Waves 4-7 produce the output: wave 4 + w computes O for token
+// tile w from the published S and U.  Per chunk c:
 //
 //   state waves                          output waves
 //   publish S (bf16 hi/lo) -> sx[c&1]
@@ -420,14 +420,20 @@ __global__ __launch_bounds__(256) void wy_prep_kernel(
 //
 // sx and ux are double-buffered by chunk parity, so the output waves work on
 // chunk c while the state waves already publish chunk c + 1; u2x is rewritten
-// only after every wave has passed the next barrier.  Every operand that does not depend on S is
-// loaded from the workspace straight into registers, one chunk ahead, each
-// group right after its last use, interleaved with the MFMAs of its phase.
+// only after every wave has passed the next barrier.  Every operand that does
+// not depend on S is loaded from the workspace straight into registers, one
+// chunk ahead, each group right after its last use, interleaved with the MFMAs
+// of its phase.
+//
+// NB = 1 gives the most blocks (the latency of one long sequence is spread over
+// every CU); NB = 2 halves the operand loads per column of S, for launches that
+// fill the GPU with blocks either way (many sequences, or many heads).
 // ---------------------------------------------------------------------------
-struct StateOps {
+template <int NB> struct StateOps {
   u32x4 w[4][2];   // W hi/lo of token tile w, d_k steps 0..3
   u32x4 kt[2][2];  // K^T of this wave's two d_k tiles, token steps 0..1
-  f32x4 u, fu;     // U' tile; e^{G_last - G} k-norm of this lane's 4 rows
+  f32x4 u[NB];     // U' tiles
+  f32x4 fu;        // e^{G_last - G} k-norm of this lane's 4 rows
   float el;        // e^{G_last}
 };
 struct OutOps {
@@ -436,32 +442,34 @@ struct OutOps {
   f32x4 fq;        // e^G q-norm of this lane's 4 rows
 };
 
-template <bool STATES, bool OBF16>
+template <bool STATES, bool OBF16, int NB>
 __global__ __launch_bounds__(512) void wy_chain_kernel(
     const float *__restrict__ s0, const Seqs sq, const unsigned char *__restrict__ wf,
     const unsigned char *__restrict__ pf, const float *__restrict__ uf, const float *__restrict__ fac,
     const unsigned char *__restrict__ ktf, const unsigned char *__restrict__ qf, void *__restrict__ o,
     float *__restrict__ fin, float *__restrict__ uw, float *__restrict__ scw, int H_qk, int H_v,
-    int d_v, int MC, int units, int grid) {
-  // S and U as published by their owner wave, in the owner's lane order.
-  // ux and u2x: the two token tiles of token step st side by side, so a reader
-  // takes its 8 contraction indices with one 16-byte load.
-  __shared__ u32x4 sx[2][4][2][64];
-  __shared__ u32x4 ux[2][2][2][64];
-  __shared__ u32x4 u2x[2][2][64];
+    int d_v, int MC, int groups) {
+  // S and U as published by their owner wave, in the owner's lane order, one
+  // 16-column tile nb after the other.  ux and u2x: the two token tiles of
+  // token step st side by side, so a reader takes its 8 contraction indices
+  // with one 16-byte load.
+  __shared__ u32x4 sx[2][4][NB][2][64];
+  __shared__ u32x4 ux[2][NB][2][2][64];
+  __shared__ u32x4 u2x[NB][2][2][64];
   constexpr int LDO = 20;  // O tile rows, fp32 (the pad spreads rows over the banks)
   __shared__ float ot[4][16 * LDO];
   if (sq.bad()) return;
-  const int u = xcd_remap(blockIdx.x, grid);
-  if (u >= units) return;
-  const int NCT = d_v / 16;
-  const int jb = u % NCT, h = (u / NCT) % H_v, n = u / (NCT * H_v);
+  const int NCT = d_v / 16;         // 16-column tiles of S
+  const int NCB = NCT / NB;         // column blocks
+  const int u = xcd_group_remap(blockIdx.x, NCB, groups);
+  if (u < 0) return;
+  const int jb = u % NCB, h = (u / NCB) % H_v, n = u / (NCB * H_v);
   const int j = h / (H_v / H_qk);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int w = wave & 3;
   const int lr = lane & 15, lg = lane >> 4;
-  const int col0 = jb * 16;
+  const int col0 = jb * 16 * NB;
   const int64_t sbase = (int64_t)(n * H_v + h) * DK;
   const int c_begin = sq.first(n), c_end = sq.first(n + 1);
   const int s_begin = sq.start(n), s_end = sq.start(n + 1);
@@ -470,16 +478,19 @@ __global__ __launch_bounds__(512) void wy_chain_kernel(
 
   if (wave < 4) {
     // ------------------------------ state waves ------------------------------
-    // S[mt] holds rows 32w + 16mt + 4lg + i, column col0 + lr.
-    f32x4 S[2];
+    // S[nb][mt] holds rows 32w + 16mt + 4lg + i, column col0 + 16nb + lr.
+    f32x4 S[NB][2];
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      S[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (s0) {
+    for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) S[mt][i] = s0[(sbase + 32 * w + 16 * mt + 4 * lg + i) * d_v + col0 + lr];
+      for (int mt = 0; mt < 2; ++mt) {
+        S[nb][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (s0) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            S[nb][mt][i] = s0[(sbase + 32 * w + 16 * mt + 4 * lg + i) * d_v + col0 + 16 * nb + lr];
+        }
       }
-    }
     // Drain the initial-state loads, so that inside the chunk loop the
     // vector-memory counter covers only the operand prefetches.
     __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
@@ -490,102 +501,120 @@ __global__ __launch_bounds__(512) void wy_chain_kernel(
     auto kp = [&](int c) {
       return reinterpret_cast<const u32x4 *>(ktf + (jslot + c) * kWyKtBytes) + 2 * w * 2 * 64 + lane;
     };
-    auto load_uf = [&](StateOps &op, int c) {
-      op.u = reinterpret_cast<const f32x4 *>(uf + (hslot + c) * (int64_t)(C * d_v))[(w * NCT + jb) * 64 + lane];
+    auto load_uf = [&](StateOps<NB> &op, int c) {
+      const f32x4 *U4 = reinterpret_cast<const f32x4 *>(uf + (hslot + c) * (int64_t)(C * d_v));
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) op.u[nb] = U4[(w * NCT + jb * NB + nb) * 64 + lane];
       const float *F = fac + (hslot + c) * kWyFac;
       op.fu = *reinterpret_cast<const f32x4 *>(F + C + 16 * w + 4 * lg);
       op.el = F[2 * C];
     };
 
-    auto chunk = [&](StateOps &op, int c, int cn) {
+    auto chunk = [&](StateOps<NB> &op, int c, int cn) {
       const int t0 = s_begin + (c - c_begin) * C;
       const int len = min(C, s_end - t0);
       // 1. publish this wave's S rows (the B operand of d_k step w)
-      {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
         u32x4 hi, lo;
-        split8(S[0], S[1], hi, lo);
-        sx[c & 1][w][0][lane] = hi;
-        sx[c & 1][w][1][lane] = lo;
+        split8(S[nb][0], S[nb][1], hi, lo);
+        sx[c & 1][w][nb][0][lane] = hi;
+        sx[c & 1][w][nb][1][lane] = lo;
         if constexpr (STATES) {
 #pragma unroll
           for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-              scw[(((int64_t)c * H_v + h) * DK + 32 * w + 16 * mt + 4 * lg + i) * d_v + col0 + lr] = S[mt][i];
+              scw[(((int64_t)c * H_v + h) * DK + 32 * w + 16 * mt + 4 * lg + i) * d_v + col0 + 16 * nb + lr] =
+                  S[nb][mt][i];
         }
       }
       __syncthreads();  // 1
       // 2. U = U' - W S for token tile w (three accumulators: hi*hi, hi*lo, lo*hi)
       const u32x4 *W4 = wp(cn);
-      f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0, a2 = a0;
+      f32x4 a0[NB], a1[NB], a2[NB];
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) a0[nb] = a1[nb] = a2[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        const bf16x8 sh = as_bf(sx[c & 1][s][0][lane]), sl = as_bf(sx[c & 1][s][1][lane]);
-        a0 = mfma_bf16(as_bf(op.w[s][0]), sh, a0);
-        a1 = mfma_bf16(as_bf(op.w[s][0]), sl, a1);
-        a2 = mfma_bf16(as_bf(op.w[s][1]), sh, a2);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          const bf16x8 sh = as_bf(sx[c & 1][s][nb][0][lane]), sl = as_bf(sx[c & 1][s][nb][1][lane]);
+          a0[nb] = mfma_bf16(as_bf(op.w[s][0]), sh, a0[nb]);
+          a1[nb] = mfma_bf16(as_bf(op.w[s][0]), sl, a1[nb]);
+          a2[nb] = mfma_bf16(as_bf(op.w[s][1]), sh, a2[nb]);
+        }
         op.w[s][0] = W4[(s * 2 + 0) * 64];
         op.w[s][1] = W4[(s * 2 + 1) * 64];
-        __builtin_amdgcn_sched_group_barrier(kDSR, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(kMFMA, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kDSR, 2 * NB, 0);
+        __builtin_amdgcn_sched_group_barrier(kMFMA, NB, 0);
         __builtin_amdgcn_sched_group_barrier(kVMR, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(kMFMA, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kMFMA, NB, 0);
         __builtin_amdgcn_sched_group_barrier(kVMR, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(kMFMA, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kMFMA, NB, 0);
       }
       //    U'' = diag(e^{G_last - G} k-norm) U; publish U and U''
-      const f32x4 uv = op.u - (a0 + a1 + a2);
-      const f32x4 u2 = uv * op.fu;
-      {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const f32x4 uv = op.u[nb] - (a0[nb] + a1[nb] + a2[nb]);
+        const f32x4 u2 = uv * op.fu;
         u32x2 hi, lo;
         split4(uv, hi, lo);
-        reinterpret_cast<u32x2 *>(&ux[c & 1][w >> 1][0][lane])[w & 1] = hi;
-        reinterpret_cast<u32x2 *>(&ux[c & 1][w >> 1][1][lane])[w & 1] = lo;
+        reinterpret_cast<u32x2 *>(&ux[c & 1][nb][w >> 1][0][lane])[w & 1] = hi;
+        reinterpret_cast<u32x2 *>(&ux[c & 1][nb][w >> 1][1][lane])[w & 1] = lo;
         split4(u2, hi, lo);
-        reinterpret_cast<u32x2 *>(&u2x[w >> 1][0][lane])[w & 1] = hi;
-        reinterpret_cast<u32x2 *>(&u2x[w >> 1][1][lane])[w & 1] = lo;
-      }
-      if constexpr (STATES) {
+        reinterpret_cast<u32x2 *>(&u2x[nb][w >> 1][0][lane])[w & 1] = hi;
+        reinterpret_cast<u32x2 *>(&u2x[nb][w >> 1][1][lane])[w & 1] = lo;
+        if constexpr (STATES) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = 16 * w + 4 * lg + i;
-          if (r < len) uw[((int64_t)(t0 + r) * H_v + h) * d_v + col0 + lr] = uv[i];
+          for (int i = 0; i < 4; ++i) {
+            const int r = 16 * w + 4 * lg + i;
+            if (r < len) uw[((int64_t)(t0 + r) * H_v + h) * d_v + col0 + 16 * nb + lr] = uv[i];
+          }
         }
       }
       const float el = op.el;
       load_uf(op, cn);
       __syncthreads();  // 2
       // 3. S <- e^{G_last} S + K^T U'' for this wave's rows
-      bf16x8 bh[2], bl[2];
+      bf16x8 bh[NB][2], bl[NB][2];
 #pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        bh[st] = as_bf(u2x[st][0][lane]);
-        bl[st] = as_bf(u2x[st][1][lane]);
-      }
-      const u32x4 *K4 = kp(cn);
-      f32x4 ah[2], al[2];  // K^T U''_hi and K^T U''_lo: four independent chains
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        ah[mt] = al[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
         for (int st = 0; st < 2; ++st) {
-          ah[mt] = mfma_bf16(as_bf(op.kt[mt][st]), bh[st], ah[mt]);
-          al[mt] = mfma_bf16(as_bf(op.kt[mt][st]), bl[st], al[mt]);
+          bh[nb][st] = as_bf(u2x[nb][st][0][lane]);
+          bl[nb][st] = as_bf(u2x[nb][st][1][lane]);
+        }
+      const u32x4 *K4 = kp(cn);
+      f32x4 ah[NB][2], al[NB][2];  // K^T U''_hi and K^T U''_lo: independent chains
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) ah[nb][mt] = al[nb][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) {
+            ah[nb][mt] = mfma_bf16(as_bf(op.kt[mt][st]), bh[nb][st], ah[nb][mt]);
+            al[nb][mt] = mfma_bf16(as_bf(op.kt[mt][st]), bl[nb][st], al[nb][mt]);
+          }
           op.kt[mt][st] = K4[(mt * 2 + st) * 64];
         }
       }
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt) S[mt] = S[mt] * el + (ah[mt] + al[mt]);
-      __builtin_amdgcn_sched_group_barrier(kDSR, 4, 0);
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) S[nb][mt] = S[nb][mt] * el + (ah[nb][mt] + al[nb][mt]);
+      __builtin_amdgcn_sched_group_barrier(kDSR, 4 * NB, 0);
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        __builtin_amdgcn_sched_group_barrier(kMFMA, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(kMFMA, 2 * NB, 0);
         __builtin_amdgcn_sched_group_barrier(kVMR, 1, 0);
       }
     };
 
     if (c_begin < c_end) {
-      StateOps op;
+      StateOps<NB> op;
       {
         const u32x4 *W4 = wp(c_begin), *K4 = kp(c_begin);
 #pragma unroll
@@ -607,9 +636,12 @@ __global__ __launch_bounds__(512) void wy_chain_kernel(
     }
     if (fin) {
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
+      for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) fin[(sbase + 32 * w + 16 * mt + 4 * lg + i) * d_v + col0 + lr] = S[mt][i];
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            fin[(sbase + 32 * w + 16 * mt + 4 * lg + i) * d_v + col0 + 16 * nb + lr] = S[nb][mt][i];
     }
   } else {
     // ------------------------------ output waves -----------------------------
@@ -631,22 +663,30 @@ __global__ __launch_bounds__(512) void wy_chain_kernel(
       __syncthreads();  // 1
       __syncthreads();  // 2
       // Q S for token tile w, from the S published for this chunk
-      f32x4 aq = {0.f, 0.f, 0.f, 0.f}, aq2 = aq;
+      f32x4 aq[NB], aq2[NB];
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const bf16x8 sh = as_bf(sx[c & 1][s][0][lane]), sl = as_bf(sx[c & 1][s][1][lane]);
-        aq = mfma_bf16(as_bf(op.q[s]), sh, aq);
-        aq2 = mfma_bf16(as_bf(op.q[s]), sl, aq2);
-      }
-      aq = (aq + aq2) * op.fq;
+      for (int nb = 0; nb < NB; ++nb) aq[nb] = aq2[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          const bf16x8 sh = as_bf(sx[c & 1][s][nb][0][lane]), sl = as_bf(sx[c & 1][s][nb][1][lane]);
+          aq[nb] = mfma_bf16(as_bf(op.q[s]), sh, aq[nb]);
+          aq2[nb] = mfma_bf16(as_bf(op.q[s]), sl, aq2[nb]);
+        }
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) aq[nb] = (aq[nb] + aq2[nb]) * op.fq;
       // O = e^G q-norm (Q S) + P U for token tile w
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
         if (st <= (w >> 1)) {
-          const bf16x8 bh = as_bf(ux[c & 1][st][0][lane]), bl = as_bf(ux[c & 1][st][1][lane]);
-          aq = mfma_bf16(as_bf(op.p[st][0]), bh, aq);
-          aq = mfma_bf16(as_bf(op.p[st][0]), bl, aq);
-          aq = mfma_bf16(as_bf(op.p[st][1]), bh, aq);
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) {
+            const bf16x8 bh = as_bf(ux[c & 1][nb][st][0][lane]), bl = as_bf(ux[c & 1][nb][st][1][lane]);
+            aq[nb] = mfma_bf16(as_bf(op.p[st][0]), bh, aq[nb]);
+            aq[nb] = mfma_bf16(as_bf(op.p[st][0]), bl, aq[nb]);
+            aq[nb] = mfma_bf16(as_bf(op.p[st][1]), bh, aq[nb]);
+          }
         }
       }
       // the next chunk's operands
@@ -661,16 +701,21 @@ __global__ __launch_bounds__(512) void wy_chain_kernel(
         // through LDS, so that each lane stores 4 consecutive columns of one
         // row: lane l takes row l%16 and columns 4(l/16) ..
 #pragma unroll
-        for (int i = 0; i < 4; ++i) ot[w][(4 * lg + i) * LDO + lr] = aq[i];
-        __builtin_amdgcn_wave_barrier();
-        const int r = 16 * w + lr;
-        if (r < len) {
+        for (int nb = 0; nb < NB; ++nb) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) ot[w][(4 * lg + i) * LDO + lr] = aq[nb][i];
+          __builtin_amdgcn_wave_barrier();
+          const int r = 16 * w + lr;
           const f32x4 x = *reinterpret_cast<const f32x4 *>(&ot[w][lr * LDO + 4 * lg]);
-          const int64_t ob = ((int64_t)(t0 + r) * H_v + h) * d_v + col0 + 4 * lg;
-          if constexpr (OBF16) {
-            *reinterpret_cast<u32x2 *>(static_cast<uint16_t *>(o) + ob) = u32x2{pk_bf16(x[0], x[1]), pk_bf16(x[2], x[3])};
-          } else {
-            *reinterpret_cast<f32x4 *>(static_cast<float *>(o) + ob) = x;
+          __builtin_amdgcn_wave_barrier();
+          if (r < len) {
+            const int64_t ob = ((int64_t)(t0 + r) * H_v + h) * d_v + col0 + 16 * nb + 4 * lg;
+            if constexpr (OBF16) {
+              *reinterpret_cast<u32x2 *>(static_cast<uint16_t *>(o) + ob) =
+                  u32x2{pk_bf16(x[0], x[1]), pk_bf16(x[2], x[3])};
+            } else {
+              *reinterpret_cast<f32x4 *>(static_cast<float *>(o) + ob) = x;
+            }
           }
         }
       }
@@ -691,6 +736,31 @@ __global__ __launch_bounds__(512) void wy_chain_kernel(
   }
 }
 
+// Compute units of the current device (cached per device).
+int device_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v == 0) {
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    cache[dev].store(v, std::memory_order_relaxed);
+  }
+  return v;
+}
+
+template <bool STATES, bool OBF16, int NB>
+hipError_t launch_chain(const Problem &p, const ChunkArgs &a, const Seqs &sq, hipStream_t st) {
+  const Workspace &w = a.ws;
+  const int groups = p.N * p.H_v, ncb = p.d_v / (16 * NB);
+  if (groups == 0 || ncb == 0) return hipSuccess;
+  const int grid = xcd_group_grid(ncb, groups);
+  hipLaunchKernelGGL((wy_chain_kernel<STATES, OBF16, NB>), dim3(grid), dim3(512), 0, st, a.s0, sq, w.wf, w.pf,
+                     w.uf, w.fac, w.ktf, w.qf, a.o, a.final_state, w.u, w.sc, p.H_qk, p.H_v, p.d_v, p.max_chunks,
+                     groups);
+  return hipGetLastError();
+}
+
 template <bool STATES, bool OBF16>
 hipError_t run_wy(const Problem &p, const ChunkArgs &a, hipStream_t st) {
   const Workspace &w = a.ws;
@@ -709,14 +779,11 @@ hipError_t run_wy(const Problem &p, const ChunkArgs &a, hipStream_t st) {
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   mark_event(a, 2, st);
-  const int units = p.N * p.H_v * (p.d_v / 16);
-  if (units > 0) {
-    const int grid = (units + 7) / 8 * 8;
-    hipLaunchKernelGGL((wy_chain_kernel<STATES, OBF16>), dim3(grid), dim3(512), 0, st, a.s0, sq, w.wf, w.pf,
-                       w.uf, w.fac, w.ktf, w.qf, a.o, a.final_state, w.u, w.sc, p.H_qk, p.H_v, p.d_v,
-                       p.max_chunks, units, grid);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-  }
+  // 32-column blocks once 16-column blocks would fill every CU twice over.
+  const bool wide = p.N * p.H_v * (p.d_v / 16) >= 2 * device_cus();
+  if ((e = wide ? launch_chain<STATES, OBF16, 2>(p, a, sq, st) : launch_chain<STATES, OBF16, 1>(p, a, sq, st)) !=
+      hipSuccess)
+    return e;
   mark_event(a, 3, st);
   if constexpr (STATES) {
     if ((e = launch_states_stream(p, a, sq, st)) != hipSuccess) return e;

@@ -217,6 +217,25 @@ def test_states_match_oracle_and_final():
     assert rel_fro(host(st[:, -1]), host(fin)) <= 1e-5
 
 
+def test_many_rows_both_paths():
+    """Four rows of 32 heads: enough (row, head) pairs that the carry runs on 32-column
+    blocks of the state (the layout for launches that fill every compute unit)."""
+    gdn = _lib()
+    inp = _bf16_case(T=150, seed=16, s0_std=0.02, B=4)
+    d = to_dev(inp)
+    heads = [0, 13, 31]
+    ref = _ref(inp, heads=heads, want_states=True)
+    o, fin = gdn.gdn_chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], initial_state=d["s0"])
+    o2, st, fin2 = gdn.gdn_states_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], initial_state=d["s0"])
+    torch.cuda.synchronize()
+    full = _ref(inp)
+    assert rel_max(host(o), full["o"]) <= TOL_BF16_O
+    assert rel_fro(host(fin), full["final"]) <= TOL_BF16_STATE
+    assert rel_max(host(o2), full["o"]) <= TOL_BF16_O
+    assert rel_fro(host(st[:, :, heads]), ref["states"]) <= TOL_BF16_STATE
+    assert rel_fro(host(fin2), full["final"]) <= TOL_BF16_STATE
+
+
 def test_empty_prompt_passes_state_through():
     gdn = _lib()
     inp = _bf16_case(T=0, seed=12, s0_std=0.02)
