@@ -519,7 +519,7 @@ __global__ __launch_bounds__(512) void carry_kernel(
 
   if (*status) return;
   const int NJB = d_v / DVB;
-  const int u = xcd_group_remap(blockIdx.x, NJB, groups);
+  const int u = xcd_group_remap(blockIdx.x, NJB * (H_v / H_qk), groups);  // (sequence, q/k head)
   if (u < 0) return;
   const int jb = u % NJB, h = (u / NJB) % H_v, n = u / (NJB * H_v);
   const int j = h / (H_v / H_qk);
@@ -874,9 +874,9 @@ static hipError_t run_t(const Problem &p, const ChunkArgs &a, hipStream_t st) {
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   mark_event(a, 2, st);
-  const int groups = p.N * p.H_v;
+  const int groups = p.N * p.H_qk;
   if (groups > 0 && p.d_v > 0) {
-    const int grid = xcd_group_grid(p.d_v / DVB, groups);
+    const int grid = xcd_group_grid(p.d_v / DVB * (p.H_v / p.H_qk), groups);
     hipLaunchKernelGGL((carry_kernel<TIn, DK, C, DVB, STATES, OBF16>), dim3(grid), dim3(512), 0, st, q, k, v,
                        a.s0, w.status, w.seq_start, w.chunk_first, reinterpret_cast<const unsigned char *>(w.tb),
                        reinterpret_cast<const unsigned char *>(w.pm), w.eg, w.eb, a.o,

@@ -154,8 +154,8 @@ struct Seqs {
 };
 
 // blockIdx -> logical work item u = g * per + r, for work made of `groups`
-// groups of `per` items that share their operands (the column blocks of one
-// (sequence, head)).  Workgroups are dealt to the 8 XCDs round robin; this keeps
+// groups of `per` items that share their operands (the column blocks of the
+// value heads of one (sequence, query/key head)).  Workgroups are dealt to the 8 XCDs round robin; this keeps
 // each group on one XCD, whose L2 then serves the group's shared reads, and
 // deals the groups themselves round robin, so that the first groups in u order
 // (the first sequences) spread over every XCD.  The grid is

@@ -461,7 +461,8 @@ __global__ __launch_bounds__(512) void wy_chain_kernel(
   if (sq.bad()) return;
   const int NCT = d_v / 16;         // 16-column tiles of S
   const int NCB = NCT / NB;         // column blocks
-  const int u = xcd_group_remap(blockIdx.x, NCB, groups);
+  // groups: (sequence, query/key head), whose value heads share K^T and Q too
+  const int u = xcd_group_remap(blockIdx.x, NCB * (H_v / H_qk), groups);
   if (u < 0) return;
   const int jb = u % NCB, h = (u / NCB) % H_v, n = u / (NCB * H_v);
   const int j = h / (H_v / H_qk);
@@ -752,9 +753,9 @@ int device_cus() {
 template <bool STATES, bool OBF16, int NB>
 hipError_t launch_chain(const Problem &p, const ChunkArgs &a, const Seqs &sq, hipStream_t st) {
   const Workspace &w = a.ws;
-  const int groups = p.N * p.H_v, ncb = p.d_v / (16 * NB);
+  const int groups = p.N * p.H_qk, ncb = p.d_v / (16 * NB);
   if (groups == 0 || ncb == 0) return hipSuccess;
-  const int grid = xcd_group_grid(ncb, groups);
+  const int grid = xcd_group_grid(ncb * (p.H_v / p.H_qk), groups);
   hipLaunchKernelGGL((wy_chain_kernel<STATES, OBF16, NB>), dim3(grid), dim3(512), 0, st, a.s0, sq, w.wf, w.pf,
                      w.uf, w.fac, w.ktf, w.qf, a.o, a.final_state, w.u, w.sc, p.H_qk, p.H_v, p.d_v, p.max_chunks,
                      groups);
