@@ -37,7 +37,8 @@ class GdnShape(ctypes.Structure):
 
 
 EXPORTS = ("gdn_chunk_fwd", "gdn_chunk_fwd_workspace", "gdn_recurrent_step", "gdn_states_fwd",
-           "gdn_states_fwd_workspace", "gdn_set_timing_events", "gdn_status_string",
+           "gdn_states_fwd_workspace", "gdn_gated_norm", "gdn_recurrent_step_gated",
+           "gdn_mixer_prologue", "gdn_set_timing_events", "gdn_status_string",
            "gdn_last_error", "gdn_version")
 
 _lib = None
@@ -64,6 +65,13 @@ def load_library(path: Optional[str] = None):
     lib.gdn_states_fwd_workspace.argtypes = [S, I]
     lib.gdn_recurrent_step.restype = ctypes.c_int
     lib.gdn_recurrent_step.argtypes = [S, P, P, P, P, P, P, P, P]
+    F = ctypes.c_float
+    lib.gdn_recurrent_step_gated.restype = ctypes.c_int
+    lib.gdn_recurrent_step_gated.argtypes = [S, P, P, P, P, P, P, P, P, F, P, P]
+    lib.gdn_gated_norm.restype = ctypes.c_int
+    lib.gdn_gated_norm.argtypes = [S, P, P, P, F, P, P]
+    lib.gdn_mixer_prologue.restype = ctypes.c_int
+    lib.gdn_mixer_prologue.argtypes = [S, P, P, P, P, P, P, P, P, P, I, P, P, P, P, P, P]
     lib.gdn_status_string.restype = ctypes.c_char_p
     lib.gdn_status_string.argtypes = [ctypes.c_int]
     lib.gdn_last_error.restype = ctypes.c_char_p
@@ -230,6 +238,108 @@ def gdn_recurrent_step(q, k, v, g, beta, state, scale=None, l2norm=False, o_dtyp
                                 _ptr(state), _ptr(o), _stream(dev))
     _check(lib, st, "gdn_recurrent_step")
     return o
+
+
+def gdn_recurrent_step_gated(q, k, v, g, beta, state, z, weight, eps=1e-6, scale=None, l2norm=False,
+                             o_dtype=torch.float32, out=None):
+    """gdn_recurrent_step with the output norm fused: returns
+    weight * o / sqrt(mean(o^2) + eps) * silu(z) per value head, [B,1,H_v,d_v]; z is
+    [B,1,H_v,d_v] in q's dtype, weight [d_v] fp32.  ``state`` is updated in place."""
+    lib = load_library()
+    dev, B, T, H_qk, H_v, d_k, d_v, N = _common(q, k, v, g, beta, None, None)
+    if T != 1:
+        raise ValueError("the decode step takes one token per sequence (T == 1)")
+    _need(state, "state", (B, H_v, d_k, d_v), torch.float32, dev)
+    _need(z, "z", (B, 1, H_v, d_v), q.dtype, dev)
+    _need(weight, "weight", (d_v,), torch.float32, dev)
+    s = _shape(q, v, 1, scale, l2norm, o_dtype, B, T)
+    if out is None:
+        out = torch.empty((B, 1, H_v, d_v), dtype=o_dtype, device=dev)
+    _need(out, "out", (B, 1, H_v, d_v), o_dtype, dev)
+    st = lib.gdn_recurrent_step_gated(ctypes.byref(s), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                      _ptr(state), _ptr(z), _ptr(weight), float(eps), _ptr(out), _stream(dev))
+    _check(lib, st, "gdn_recurrent_step_gated")
+    return out
+
+
+def gdn_gated_norm(y, z, weight, eps=1e-6, out=None):
+    """The mixer's output norm, per (token, value head): weight * y / sqrt(mean(y^2) + eps)
+    * silu(z).  y [B,T,H_v,d_v] fp32 or bf16 (the delta rule's o); z [B,T,H_v,d_v] fp32 or
+    bf16; weight [d_v] fp32.  ``out`` (y's dtype) may be y itself."""
+    lib = load_library()
+    dev = y.device
+    if dev.type != "cuda":
+        raise ValueError("libgdn runs on the GPU: tensors must be on a cuda (HIP) device")
+    if y.dim() != 4:
+        raise ValueError("y must be [B, T, H_v, d_v]")
+    B, T, H_v, d_v = y.shape
+    if y.dtype not in _DT or z.dtype not in _DT:
+        raise ValueError("y and z must be float32 or bfloat16")
+    _need(y, "y", (B, T, H_v, d_v), y.dtype, dev)
+    _need(z, "z", (B, T, H_v, d_v), z.dtype, dev)
+    _need(weight, "weight", (d_v,), torch.float32, dev)
+    if out is None:
+        out = torch.empty_like(y)
+    _need(out, "out", (B, T, H_v, d_v), y.dtype, dev)
+    s = GdnShape(B, T, 1, H_v, 1, d_v, 1, 1.0, _DT[z.dtype], _DT[y.dtype], 0)
+    st = lib.gdn_gated_norm(ctypes.byref(s), _ptr(y), _ptr(z), _ptr(weight), float(eps), _ptr(out),
+                            _stream(dev))
+    _check(lib, st, "gdn_gated_norm")
+    return out
+
+
+def gdn_mixer_prologue(x, conv_w, a, b, A_log, dt_bias, H_qk, d_k, H_v, d_v, conv_state=None,
+                       cu_seqlens=None, update_conv_state=False, conv_state_out=None):
+    """The mixer's steps before the delta rule: q, k, v = split(silu(conv1d(x))) with a
+    causal width-4 depthwise filter, beta = sigmoid(b), g = -exp(A_log) softplus(a + dt_bias).
+
+    x [B,T,C] fp32 or bf16 with C = 2 H_qk d_k + H_v d_v (channels q | k | v); conv_w [C,4]
+    fp32 (tap 3 multiplies the current token); a, b [B,T,H_v] fp32; A_log, dt_bias [H_v]
+    fp32; conv_state [N,C,3] fp32 or None (zeros).  With update_conv_state the new
+    convolution state is written back into conv_state (in place); with conv_state_out it
+    goes there.  Returns (q, k, v, g, beta, conv_state_out or None).
+    """
+    lib = load_library()
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError("libgdn runs on the GPU: tensors must be on a cuda (HIP) device")
+    if x.dim() != 3 or x.dtype not in _DT:
+        raise ValueError("x must be [B, T, C] float32 or bfloat16")
+    B, T, C = x.shape
+    if C != 2 * H_qk * d_k + H_v * d_v:
+        raise ValueError(f"x has {C} channels, expected 2*H_qk*d_k + H_v*d_v = {2 * H_qk * d_k + H_v * d_v}")
+    _need(x, "x", (B, T, C), x.dtype, dev)
+    _need(conv_w, "conv_w", (C, 4), torch.float32, dev)
+    _need(a, "a", (B, T, H_v), torch.float32, dev)
+    _need(b, "b", (B, T, H_v), torch.float32, dev)
+    _need(A_log, "A_log", (H_v,), torch.float32, dev)
+    _need(dt_bias, "dt_bias", (H_v,), torch.float32, dev)
+    N = B
+    if cu_seqlens is not None:
+        if B != 1:
+            raise ValueError("packed sequences (cu_seqlens) need B == 1")
+        _need(cu_seqlens, "cu_seqlens", (cu_seqlens.numel(),), torch.int32, dev)
+        N = cu_seqlens.numel() - 1
+    if conv_state is not None:
+        _need(conv_state, "conv_state", (N, C, 3), torch.float32, dev)
+    if update_conv_state:
+        if conv_state is None:
+            raise ValueError("update_conv_state needs conv_state")
+        conv_state_out = conv_state
+    if conv_state_out is not None:
+        _need(conv_state_out, "conv_state_out", (N, C, 3), torch.float32, dev)
+    q = torch.empty((B, T, H_qk, d_k), dtype=x.dtype, device=dev)
+    k = torch.empty((B, T, H_qk, d_k), dtype=x.dtype, device=dev)
+    v = torch.empty((B, T, H_v, d_v), dtype=x.dtype, device=dev)
+    g = torch.empty((B, T, H_v), dtype=torch.float32, device=dev)
+    beta = torch.empty((B, T, H_v), dtype=torch.float32, device=dev)
+    s = GdnShape(B, T, H_qk, H_v, d_k, d_v, 1, 1.0, _DT[x.dtype], GDN_F32, 0)
+    nseq = N if cu_seqlens is not None else 0
+    st = lib.gdn_mixer_prologue(ctypes.byref(s), _ptr(x), _ptr(conv_w), _ptr(conv_state), _ptr(conv_state_out),
+                                _ptr(a), _ptr(b), _ptr(A_log), _ptr(dt_bias), _ptr(cu_seqlens), nseq,
+                                _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _stream(dev))
+    _check(lib, st, "gdn_mixer_prologue")
+    return q, k, v, g, beta, conv_state_out
 
 
 def plan_status(workspace: torch.Tensor) -> int:

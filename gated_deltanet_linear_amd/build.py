@@ -17,7 +17,7 @@ INCLUDE = os.path.join(ROOT, "include")
 OUT = os.path.join(PKG, "libgdn.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
-SOURCES = ["gdn_api.cpp", "gdn_step.hip", "gdn_chunk.hip", "gdn_wy.hip"]
+SOURCES = ["gdn_api.cpp", "gdn_step.hip", "gdn_chunk.hip", "gdn_wy.hip", "gdn_mixer.hip"]
 
 # Packed-fp32 VALU forms are kept out of the generated code (the compiler would
 # otherwise form v_pk_{add,mul,fma}_f32 from ordinary float code).

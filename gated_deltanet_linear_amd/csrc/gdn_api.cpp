@@ -53,8 +53,10 @@ struct Span {
 
 size_t esize(int dt) { return dt == GDN_BF16 ? 2 : 4; }
 
-// Shape checks shared by every entry point; fills p.
-gdn_status check_shape(const gdn_shape *s, bool packed, int32_t num_seqs, bool step, gdn::Problem &p) {
+// Shape checks shared by every entry point; fills p.  mode: 0 chunked path, 1 decode
+// step (T == 1), 2 token-wise mixer steps (no chunk).
+gdn_status check_shape(const gdn_shape *s, bool packed, int32_t num_seqs, int mode, gdn::Problem &p) {
+  const bool step = mode == 1;
   if (!s) return fail(GDN_ERR_NULL, "shape is NULL");
   if (s->dtype != GDN_F32 && s->dtype != GDN_BF16) return fail(GDN_ERR_DTYPE, "dtype %d", s->dtype);
   if (s->o_dtype != GDN_F32 && s->o_dtype != GDN_BF16) return fail(GDN_ERR_DTYPE, "o_dtype %d", s->o_dtype);
@@ -66,7 +68,7 @@ gdn_status check_shape(const gdn_shape *s, bool packed, int32_t num_seqs, bool s
   if (!(s->scale == s->scale)) return fail(GDN_ERR_SHAPE, "scale is NaN");
   if (step) {
     if (s->T != 1) return fail(GDN_ERR_SHAPE, "the decode step takes T == 1, got %d", s->T);
-  } else if (s->chunk <= 0) {
+  } else if (mode == 0 && s->chunk <= 0) {
     return fail(GDN_ERR_SHAPE, "chunk=%d", s->chunk);
   }
   if (packed) {
@@ -82,7 +84,7 @@ gdn_status check_shape(const gdn_shape *s, bool packed, int32_t num_seqs, bool s
   p.H_v = s->H_v;
   p.d_k = s->d_k;
   p.d_v = s->d_v;
-  p.C = step ? 1 : s->chunk;
+  p.C = mode == 0 ? s->chunk : 1;
   p.packed = packed;
   p.N = packed ? num_seqs : s->B;
   p.T_tot = (int)T_tot;
@@ -91,7 +93,7 @@ gdn_status check_shape(const gdn_shape *s, bool packed, int32_t num_seqs, bool s
   p.o_dtype = s->o_dtype;
   p.l2norm = (s->flags & GDN_QK_L2NORM) != 0;
   p.max_chunks = 0;
-  if (!step) {
+  if (mode == 0) {
     const int64_t mc = packed ? (T_tot + p.C - 1) / p.C + p.N : (int64_t)p.B * ((p.T + p.C - 1) / p.C);
     if (mc * p.H_v > (1LL << 30)) return fail(GDN_ERR_SHAPE, "too many chunks");
     p.max_chunks = (int)mc;
@@ -128,7 +130,7 @@ gdn_status chunked_common(const gdn_shape *s, const void *q, const void *k, cons
                           int32_t num_seqs, void *o, float *states, float *final_state, void *workspace,
                           size_t workspace_bytes, hipStream_t stream, bool with_states) {
   gdn::Problem p;
-  gdn_status st = check_shape(s, cu_seqlens != nullptr, num_seqs, false, p);
+  gdn_status st = check_shape(s, cu_seqlens != nullptr, num_seqs, 0, p);
   if (st != GDN_OK) return st;
   if (!gdn::chunk_path_supported(p))
     return fail(GDN_ERR_UNSUPPORTED, "no chunked kernel for dtype=%d d_k=%d d_v=%d chunk=%d", p.dtype, p.d_k,
@@ -226,7 +228,7 @@ static size_t workspace_query(const gdn_shape *s, int32_t num_seqs, bool states)
   try {
     const std::string keep = g_last_error;  // a query never changes the last error
     gdn::Problem p;
-    const gdn_status st = check_shape(s, num_seqs > 0, num_seqs, false, p);
+    const gdn_status st = check_shape(s, num_seqs > 0, num_seqs, 0, p);
     g_last_error = keep;
     if (st != GDN_OK) return 0;
     return gdn::workspace_layout(p, states, nullptr).bytes;
@@ -271,7 +273,7 @@ gdn_status gdn_recurrent_step(const gdn_shape *s, const void *q, const void *k, 
                               const float *beta, float *state, void *o, hipStream_t stream) {
   try {
     gdn::Problem p;
-    gdn_status st = check_shape(s, false, 0, true, p);
+    gdn_status st = check_shape(s, false, 0, 1, p);
     if (st != GDN_OK) return st;
     if (!gdn::step_supported(p))
       return fail(GDN_ERR_UNSUPPORTED, "no decode kernel for d_k=%d d_v=%d", p.d_k, p.d_v);
@@ -293,6 +295,135 @@ gdn_status gdn_recurrent_step(const gdn_shape *s, const void *q, const void *k, 
     if (t.o.overlaps(sst)) return fail(GDN_ERR_ALIAS, "o overlaps state");
     gdn::StepArgs a{q, k, v, g, beta, state, o};
     const hipError_t e = gdn::launch_recurrent_step(p, a, stream);
+    if (e != hipSuccess) return fail(GDN_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+    g_last_error.clear();
+    return GDN_OK;
+  } catch (...) {
+    return fail(GDN_ERR_HIP, "internal error");
+  }
+}
+
+gdn_status gdn_recurrent_step_gated(const gdn_shape *s, const void *q, const void *k, const void *v,
+                                    const float *g, const float *beta, float *state, const void *z,
+                                    const float *weight, float eps, void *out, hipStream_t stream) {
+  try {
+    gdn::Problem p;
+    gdn_status st = check_shape(s, false, 0, 1, p);
+    if (st != GDN_OK) return st;
+    if (!gdn::step_supported(p))
+      return fail(GDN_ERR_UNSUPPORTED, "no decode kernel for d_k=%d d_v=%d", p.d_k, p.d_v);
+    if (!(eps >= 0.0f) || eps > 1e30f) return fail(GDN_ERR_SHAPE, "eps=%g", (double)eps);
+    if (p.B > 0 && (!q || !k || !v || !g || !beta || !state || !z || !weight || !out))
+      return fail(GDN_ERR_NULL, "q, k, v, g, beta, state, z, weight and out are required");
+    const Arg args[] = {{q, "q", esize(p.dtype)}, {k, "k", esize(p.dtype)},     {v, "v", esize(p.dtype)},
+                        {g, "g", 4},              {beta, "beta", 4},            {state, "state", 16},
+                        {z, "z", esize(p.dtype)}, {weight, "weight", 4},        {out, "out", 4 * esize(p.o_dtype)}};
+    if ((st = check_alignment(args)) != GDN_OK) return st;
+    const Tensors t = spans(p, q, k, v, g, beta, nullptr, nullptr, out, nullptr, nullptr, nullptr, 0);
+    const Span sst(state, (size_t)p.B * p.H_v * p.d_k * p.d_v * sizeof(float));
+    const Span sz(z, (size_t)p.B * p.H_v * p.d_v * esize(p.dtype)), sw(weight, (size_t)p.d_v * sizeof(float));
+    const Span ins[] = {t.q, t.k, t.v, t.g, t.beta, sz, sw};
+    const char *in_names[] = {"q", "k", "v", "g", "beta", "z", "weight"};
+    for (int i = 0; i < 7; ++i) {
+      if (sst.overlaps(ins[i])) return fail(GDN_ERR_ALIAS, "state overlaps %s", in_names[i]);
+      if (t.o.overlaps(ins[i])) return fail(GDN_ERR_ALIAS, "out overlaps %s", in_names[i]);
+    }
+    if (t.o.overlaps(sst)) return fail(GDN_ERR_ALIAS, "out overlaps state");
+    gdn::StepArgs a{q, k, v, g, beta, state, out, z, weight, eps};
+    const hipError_t e = gdn::launch_recurrent_step(p, a, stream);
+    if (e != hipSuccess) return fail(GDN_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+    g_last_error.clear();
+    return GDN_OK;
+  } catch (...) {
+    return fail(GDN_ERR_HIP, "internal error");
+  }
+}
+
+gdn_status gdn_gated_norm(const gdn_shape *s, const void *y, const void *z, const float *weight, float eps,
+                          void *out, hipStream_t stream) {
+  try {
+    gdn::Problem p;
+    gdn_status st = check_shape(s, false, 0, 2, p);
+    if (st != GDN_OK) return st;
+    if (!gdn::norm_supported(p)) return fail(GDN_ERR_UNSUPPORTED, "no norm kernel for d_v=%d", p.d_v);
+    if (!(eps >= 0.0f) || eps > 1e30f) return fail(GDN_ERR_SHAPE, "eps=%g", (double)eps);
+    const size_t rows = (size_t)p.T_tot * p.H_v;
+    if (rows > 0 && (!y || !z || !weight || !out)) return fail(GDN_ERR_NULL, "y, z, weight and out are required");
+    const Arg args[] = {{y, "y", 4 * esize(p.o_dtype)},
+                        {z, "z", 4 * esize(p.dtype)},
+                        {weight, "weight", 16},
+                        {out, "out", 4 * esize(p.o_dtype)}};
+    if ((st = check_alignment(args)) != GDN_OK) return st;
+    const Span sy(y, rows * p.d_v * esize(p.o_dtype)), so(out, rows * p.d_v * esize(p.o_dtype));
+    const Span sz(z, rows * p.d_v * esize(p.dtype)), sw(weight, (size_t)p.d_v * sizeof(float));
+    if (so.overlaps(sy) && !(so.lo == sy.lo && so.hi == sy.hi))
+      return fail(GDN_ERR_ALIAS, "out overlaps y other than exactly (in place)");
+    if (so.overlaps(sz)) return fail(GDN_ERR_ALIAS, "out overlaps z");
+    if (so.overlaps(sw)) return fail(GDN_ERR_ALIAS, "out overlaps weight");
+    gdn::NormArgs a{y, z, weight, eps, out};
+    const hipError_t e = gdn::launch_gated_norm(p, a, stream);
+    if (e != hipSuccess) return fail(GDN_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+    g_last_error.clear();
+    return GDN_OK;
+  } catch (...) {
+    return fail(GDN_ERR_HIP, "internal error");
+  }
+}
+
+gdn_status gdn_mixer_prologue(const gdn_shape *s, const void *x, const float *conv_w,
+                              const float *conv_state_in, float *conv_state_out, const float *a_in,
+                              const float *b_in, const float *A_log, const float *dt_bias,
+                              const int32_t *cu_seqlens, int32_t num_seqs, void *q, void *k, void *v,
+                              float *g, float *beta, hipStream_t stream) {
+  try {
+    gdn::Problem p;
+    gdn_status st = check_shape(s, cu_seqlens != nullptr, num_seqs, 2, p);
+    if (st != GDN_OK) return st;
+    if (!gdn::prologue_supported(p))
+      return fail(GDN_ERR_UNSUPPORTED, "no prologue kernel for d_k=%d d_v=%d (multiples of 4)", p.d_k, p.d_v);
+    if (p.packed && p.T_tot > 0 && p.N < 1) return fail(GDN_ERR_SHAPE, "num_seqs=%d with tokens", p.N);
+    const size_t T = p.T_tot, es = esize(p.dtype);
+    const size_t nq = (size_t)p.H_qk * p.d_k, nv = (size_t)p.H_v * p.d_v, Cch = 2 * nq + nv;
+    if (Cch > (1u << 28)) return fail(GDN_ERR_SHAPE, "%zu channels", Cch);
+    if (T > 0 && (!x || !conv_w || !a_in || !b_in || !A_log || !dt_bias || !q || !k || !v || !g || !beta))
+      return fail(GDN_ERR_NULL, "x, conv_w, a, b, A_log, dt_bias, q, k, v, g and beta are required");
+    const Arg args[] = {{x, "x", 4 * es},         {conv_w, "conv_w", 16},    {conv_state_in, "conv_state_in", 4},
+                        {conv_state_out, "conv_state_out", 4}, {a_in, "a", 4}, {b_in, "b", 4},
+                        {A_log, "A_log", 4},     {dt_bias, "dt_bias", 4},   {cu_seqlens, "cu_seqlens", 4},
+                        {q, "q", 4 * es},        {k, "k", 4 * es},          {v, "v", 4 * es},
+                        {g, "g", 4},             {beta, "beta", 4}};
+    if ((st = check_alignment(args)) != GDN_OK) return st;
+    const size_t cs_bytes = (size_t)p.N * Cch * 3 * sizeof(float);
+    const Span ins[] = {Span(x, T * Cch * es),
+                        Span(conv_w, Cch * 4 * sizeof(float)),
+                        Span(conv_state_in, cs_bytes),
+                        Span(a_in, T * p.H_v * sizeof(float)),
+                        Span(b_in, T * p.H_v * sizeof(float)),
+                        Span(A_log, (size_t)p.H_v * sizeof(float)),
+                        Span(dt_bias, (size_t)p.H_v * sizeof(float)),
+                        Span(cu_seqlens, ((size_t)p.N + 1) * sizeof(int32_t))};
+    const char *in_names[] = {"x", "conv_w", "conv_state_in", "a", "b", "A_log", "dt_bias", "cu_seqlens"};
+    struct Out {
+      Span s;
+      const char *name;
+    } outs[] = {{Span(q, T * nq * es), "q"},
+                {Span(k, T * nq * es), "k"},
+                {Span(v, T * nv * es), "v"},
+                {Span(g, T * p.H_v * sizeof(float)), "g"},
+                {Span(beta, T * p.H_v * sizeof(float)), "beta"},
+                {Span(conv_state_out, cs_bytes), "conv_state_out"}};
+    for (int o = 0; o < 6; ++o) {
+      for (int i = 0; i < 8; ++i) {
+        if (!outs[o].s.overlaps(ins[i])) continue;
+        const bool inplace = o == 5 && i == 2 && outs[o].s.lo == ins[i].lo && outs[o].s.hi == ins[i].hi;
+        if (!inplace) return fail(GDN_ERR_ALIAS, "%s overlaps %s", outs[o].name, in_names[i]);
+      }
+      for (int o2 = o + 1; o2 < 6; ++o2)
+        if (outs[o].s.overlaps(outs[o2].s)) return fail(GDN_ERR_ALIAS, "%s overlaps %s", outs[o].name, outs[o2].name);
+    }
+    gdn::PrologueArgs a{x, conv_w, conv_state_in, conv_state_out, a_in, b_in, A_log, dt_bias, cu_seqlens,
+                        q, k, v, g, beta};
+    const hipError_t e = gdn::launch_prologue(p, a, stream);
     if (e != hipSuccess) return fail(GDN_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
     g_last_error.clear();
     return GDN_OK;

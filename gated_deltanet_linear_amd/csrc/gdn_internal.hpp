@@ -96,8 +96,37 @@ struct StepArgs {
   const float *g, *beta;
   float *state;
   void *o;
+  // optional fused output norm: o <- weight * o / sqrt(mean(o^2) + eps) * silu(z)
+  const void *z = nullptr;
+  const float *weight = nullptr;
+  float eps = 0.0f;
 };
 hipError_t launch_recurrent_step(const Problem &p, const StepArgs &a, hipStream_t stream);
 bool step_supported(const Problem &p);
+
+// The mixer's steps around the delta rule (gdn_mixer.hip).
+struct NormArgs {
+  const void *y;        // [T_tot, H_v, d_v] o_dtype
+  const void *z;        // [T_tot, H_v, d_v] dtype
+  const float *weight;  // [d_v]
+  float eps;
+  void *out;            // [T_tot, H_v, d_v] o_dtype, may be y
+};
+bool norm_supported(const Problem &p);
+hipError_t launch_gated_norm(const Problem &p, const NormArgs &a, hipStream_t stream);
+
+struct PrologueArgs {
+  const void *x;          // [T_tot, 2 H_qk d_k + H_v d_v] dtype
+  const float *conv_w;    // [channels, 4]
+  const float *cs_in;     // [N, channels, 3] or null
+  float *cs_out;          // [N, channels, 3] or null; may be cs_in
+  const float *a, *b;     // [T_tot, H_v]
+  const float *A_log, *dt_bias;  // [H_v]
+  const int32_t *cu;      // cu_seqlens or null
+  void *q, *k, *v;        // dtype
+  float *g, *beta;        // [T_tot, H_v]
+};
+bool prologue_supported(const Problem &p);
+hipError_t launch_prologue(const Problem &p, const PrologueArgs &a, hipStream_t stream);
 
 }  // namespace gdn

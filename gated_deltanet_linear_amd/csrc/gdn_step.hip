@@ -10,6 +10,11 @@
 //   S <- a S + k d^T                in place
 //   o = a r + (k . q) d             = S_new^T q, read after the write
 //
+// and, in the gated variant, the mixer's output norm on the spot (the same
+// page's note "The DeltaNet mixer": norm(y, gate=silu(z)) with gain weight):
+//
+//   o <- weight * o / sqrt(mean(o^2) + eps) * silu(z)   over the head's d_v values
+//
 // The step is a pure HBM stream (0.74 FLOP per byte): one workgroup per
 // (b, h) of up to 1024 threads; each thread keeps a 4-column x (d_k / row
 // groups)-row strip of S in registers between the read and the write, so S
@@ -32,11 +37,12 @@ template <int DK, int DV> struct StepCfg {
   static_assert(NT % 64 == 0 || NT == CG * RG, "whole waves");
 };
 
-template <int DK, int DV, typename TIn, bool OBF16>
+template <int DK, int DV, typename TIn, bool OBF16, bool GN>
 __global__ __launch_bounds__((StepCfg<DK, DV>::NT)) void step_kernel(
     const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__restrict__ v,
     const float *__restrict__ g, const float *__restrict__ beta, float *__restrict__ state,
-    void *__restrict__ o, int H_qk, int H_v, float scale, int l2norm) {
+    void *__restrict__ o, int H_qk, int H_v, float scale, int l2norm, const TIn *__restrict__ z,
+    const float *__restrict__ wn, float eps) {
   using Cfg = StepCfg<DK, DV>;
   constexpr int CG = Cfg::CG, RG = Cfg::RG, RPT = Cfg::RPT, NW = Cfg::NW;
 
@@ -140,7 +146,20 @@ __global__ __launch_bounds__((StepCfg<DK, DV>::NT)) void step_kernel(
     __builtin_nontemporal_store(alpha * S[s] + kk * d, reinterpret_cast<f32x4 *>(Sp + (int64_t)row * DV + 4 * cg));
   }
   if (rg == 0) {
-    const f32x4 out = alpha * r + kq * d;
+    f32x4 out = alpha * r + kq * d;
+    if constexpr (GN) {
+      // the head's d_v outputs sit in lanes 0 .. CG-1 of wave 0, 4 per lane
+      float ss = out[0] * out[0] + out[1] * out[1] + out[2] * out[2] + out[3] * out[3];
+#pragma unroll
+      for (int m = 1; m < CG; m <<= 1) ss += wave_xor(ss, m);
+      const float rs = rsqrtf(ss * (1.0f / DV) + eps);
+      const int64_t zo = (int64_t)bh * DV + 4 * cg;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const float zc = Elem<TIn>::get(z, zo + c);
+        out[c] = wn[4 * cg + c] * (out[c] * rs) * (zc / (1.0f + __expf(-zc)));
+      }
+    }
     if constexpr (OBF16) {
       uint16_t *op = reinterpret_cast<uint16_t *>(o) + (int64_t)bh * DV + 4 * cg;
       uint2 pk;
@@ -157,10 +176,18 @@ template <int DK, int DV, typename TIn, bool OBF16>
 static hipError_t launch_step_t(const Problem &p, const StepArgs &a, hipStream_t st) {
   const int grid = p.B * p.H_v;
   if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL((step_kernel<DK, DV, TIn, OBF16>), dim3(grid), dim3(StepCfg<DK, DV>::NT), 0, st,
-                     static_cast<const TIn *>(a.q), static_cast<const TIn *>(a.k),
-                     static_cast<const TIn *>(a.v), a.g, a.beta, a.state, a.o, p.H_qk, p.H_v, p.scale,
-                     p.l2norm ? 1 : 0);
+  if (a.z) {
+    hipLaunchKernelGGL((step_kernel<DK, DV, TIn, OBF16, true>), dim3(grid), dim3(StepCfg<DK, DV>::NT), 0, st,
+                       static_cast<const TIn *>(a.q), static_cast<const TIn *>(a.k),
+                       static_cast<const TIn *>(a.v), a.g, a.beta, a.state, a.o, p.H_qk, p.H_v, p.scale,
+                       p.l2norm ? 1 : 0, static_cast<const TIn *>(a.z), a.weight, a.eps);
+  } else {
+    hipLaunchKernelGGL((step_kernel<DK, DV, TIn, OBF16, false>), dim3(grid), dim3(StepCfg<DK, DV>::NT), 0, st,
+                       static_cast<const TIn *>(a.q), static_cast<const TIn *>(a.k),
+                       static_cast<const TIn *>(a.v), a.g, a.beta, a.state, a.o, p.H_qk, p.H_v, p.scale,
+                       p.l2norm ? 1 : 0, static_cast<const TIn *>(nullptr), static_cast<const float *>(nullptr),
+                       0.0f);
+  }
   return hipGetLastError();
 }
 

@@ -177,3 +177,47 @@ def make_decode_pool(w: Workload, seed: int = 0, pool: Optional[int] = None, B: 
         "g": (-_softplus(gn + w.g_shift)).astype(np.float32),
         "s0": s0, "dtype": w.dtype,
     }
+
+
+def make_mixer_inputs(w: Workload, seed: int = 0, T: Optional[int] = None, B: Optional[int] = None,
+                      lengths: Optional[Tuple[int, ...]] = None, with_conv_state: bool = False):
+    """Inputs of the mixer steps around the delta rule, for workload ``w``'s head layout.
+
+    Returns a dict of numpy arrays:
+      ``x``        [B, T, C] in ``w.dtype`` (as float32), C = 2 H_qk d_k + H_v d_v: the
+                   convolution's input, channels q | k | v, ~ N(0, 1);
+      ``conv_w``   [C, 4] float32 ~ N(0, 0.5^2);
+      ``a``, ``b`` [B, T, H_v] float32 ~ N(0, 1);
+      ``A_log``    [H_v] float32, log of U(1, 16);
+      ``dt_bias``  [H_v] float32, log(expm1(dt)) with dt log-uniform in [1e-3, 1e-1];
+      ``z``        [B, T, H_v, d_v] in ``w.dtype`` ~ N(0, 1): the output gate's input;
+      ``norm_w``   [d_v] float32 ~ 1 + N(0, 0.1^2): the output norm's gain;
+      ``conv_state`` [N, C, 3] float32 (dtype-exact values) ~ N(0, 1), or None;
+      ``cu_seqlens`` int32 [N+1] or None.
+    """
+    if lengths is None and w.lengths is not None and T is None:
+        lengths = w.lengths
+    if lengths is not None:
+        B_, T_ = 1, int(sum(lengths))
+    else:
+        B_ = w.B if B is None else B
+        T_ = w.T if T is None else T
+    C = 2 * w.H_qk * w.d_k + w.H_v * w.d_v
+    N = len(lengths) if lengths is not None else B_
+    rng = np.random.default_rng(seed)
+    x = _normal(rng, (B_, T_, C))
+    conv_w = (_normal(rng, (C, 4)) * np.float32(0.5)).astype(np.float32)
+    a = _normal(rng, (B_, T_, w.H_v))
+    b = _normal(rng, (B_, T_, w.H_v))
+    A_log = np.log(rng.uniform(1.0, 16.0, size=w.H_v)).astype(np.float32)
+    dt = np.exp(rng.uniform(np.log(1e-3), np.log(1e-1), size=w.H_v))
+    dt_bias = np.log(np.expm1(dt)).astype(np.float32)
+    z = _normal(rng, (B_, T_, w.H_v, w.d_v))
+    norm_w = (1.0 + 0.1 * _normal(rng, (w.d_v,))).astype(np.float32)
+    cs = round_to(_normal(rng, (N, C, 3)), w.dtype) if with_conv_state else None
+    out = {"x": round_to(x, w.dtype), "conv_w": conv_w, "a": a, "b": b, "A_log": A_log, "dt_bias": dt_bias,
+           "z": round_to(z, w.dtype), "norm_w": norm_w, "conv_state": cs, "cu_seqlens": None,
+           "dtype": w.dtype}
+    if lengths is not None:
+        out["cu_seqlens"] = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    return out

@@ -158,6 +158,86 @@ gdn_status gdn_states_fwd(const gdn_shape *s, const void *q, const void *k,
 size_t gdn_states_fwd_workspace(const gdn_shape *s, int32_t num_seqs);
 
 /*
+ * The mixer's steps around the delta rule (Qwen3.5 text encyclopedia page,
+ * note "The DeltaNet mixer"; Qwen3-Next encyclopedia page, same note):
+ *
+ *     q, k, v = split(silu(conv1d(x)))       causal, width 4, one filter per channel
+ *     beta    = sigmoid(b)
+ *     g       = -exp(A_log) * softplus(a + dt_bias)
+ *     y, S    = delta_rule(...)                (the entry points above)
+ *     out     = norm(y, gate = silu(z))        gain weight
+ *
+ * The module listing on the first page gives the convolution as depthwise, kernel
+ * size 4, padding 3, no bias; the note "The readout is the plain projection"
+ * gives the output norm's gain as its weight (not 1 + weight).
+ */
+
+/*
+ * gdn_gated_norm: the output norm, per (token, value head) over its d_v values:
+ *
+ *     out = weight * y / sqrt(mean(y^2) + eps) * silu(z),   silu(x) = x sigmoid(x)
+ *
+ *   y       [B, T, H_v, d_v]  s->o_dtype (the o of gdn_chunk_fwd / gdn_states_fwd)
+ *   z       [B, T, H_v, d_v]  s->dtype   (the gate's input, in_proj_z's output)
+ *   weight  [d_v]             float32, shared by the heads
+ *   eps     >= 0 (the family's norms use 1e-6)
+ *   out     [B, T, H_v, d_v]  s->o_dtype (written); may be y itself (in place),
+ *           must not overlap z or weight
+ * Uses s->B, T, H_v, d_v, dtype, o_dtype; built for d_v in {16, 32, 64, 128, 256}.
+ * y, z and out are read and written 4 elements at a time (aligned to 4 elements),
+ * weight as float4 (16-byte aligned).
+ */
+gdn_status gdn_gated_norm(const gdn_shape *s, const void *y, const void *z,
+                          const float *weight, float eps, void *out,
+                          hipStream_t stream);
+
+/*
+ * gdn_recurrent_step_gated: gdn_recurrent_step with the output norm fused into
+ * the step kernel: writes out = gdn_gated_norm of the step's o, which never
+ * reaches memory.
+ *
+ *   z       [B, 1, H_v, d_v]  dtype
+ *   weight  [d_v]             float32
+ *   out     [B, 1, H_v, d_v]  o_dtype (written); must not overlap any input
+ * Other arguments as gdn_recurrent_step.
+ */
+gdn_status gdn_recurrent_step_gated(const gdn_shape *s, const void *q, const void *k,
+                                    const void *v, const float *g, const float *beta,
+                                    float *state, const void *z, const float *weight,
+                                    float eps, void *out, hipStream_t stream);
+
+/*
+ * gdn_mixer_prologue: the steps before the delta rule, in one pass over x.
+ *
+ *   x               [B, T, C] dtype, C = 2 H_qk d_k + H_v d_v: in_proj_qkv's output,
+ *                   channels q (H_qk d_k), then k (H_qk d_k), then v (H_v d_v)
+ *   conv_w          [C, 4] float32, the depthwise causal filter; tap 3 multiplies the
+ *                   current token, tap i the token 3 - i before it
+ *   conv_state_in   [N, C, 3] float32, the three inputs before each sequence (oldest
+ *                   first), or NULL for zeros
+ *   conv_state_out  [N, C, 3] float32 (written): the last three inputs each sequence
+ *                   has seen, counting its conv_state_in; or NULL.  It may be
+ *                   conv_state_in itself (in-place update of a decode cache)
+ *   a, b            [B, T, H_v] float32: in_proj_a and in_proj_b outputs
+ *   A_log, dt_bias  [H_v] float32
+ *   cu_seqlens, num_seqs as gdn_chunk_fwd (N = num_seqs if cu_seqlens else B);
+ *                   a decode step is B rows of T = 1 with conv_state_in/out
+ *   q, k            [B, T, H_qk, d_k] dtype (written): silu(conv(x)) split
+ *   v               [B, T, H_v, d_v]  dtype (written)
+ *   g, beta         [B, T, H_v] float32 (written)
+ * q and k leave unnormalised and unscaled: the delta-rule entry points apply the
+ * l2 norm (GDN_QK_L2NORM) and the scale.  Needs d_k and d_v multiples of 4; x,
+ * q, k, v aligned to 4 elements, conv_w to 16 bytes.  No output may overlap an
+ * input, except conv_state_out == conv_state_in exactly.
+ */
+gdn_status gdn_mixer_prologue(const gdn_shape *s, const void *x, const float *conv_w,
+                              const float *conv_state_in, float *conv_state_out,
+                              const float *a, const float *b, const float *A_log,
+                              const float *dt_bias, const int32_t *cu_seqlens,
+                              int32_t num_seqs, void *q, void *k, void *v, float *g,
+                              float *beta, hipStream_t stream);
+
+/*
  * gdn_set_timing_events: benchmark instrumentation.  While `events` is
  * non-NULL, every gdn_chunk_fwd / gdn_states_fwd call made on this host thread
  * records events[0] on its stream before its first kernel and events[i] right
