@@ -924,14 +924,14 @@ Workspace workspace_layout(const Problem &p, bool states, void *base) {
   const size_t cf = take(sizeof(int32_t) * ((size_t)p.N + 1));
   const size_t cc = (size_t)p.max_chunks * p.H_v;
   const bool wy = p.dtype == GDN_BF16;
-  size_t tb = 0, pm = 0, eg = 0, eb = 0, wf = 0, pf = 0, uf = 0, fc = 0, kt = 0, qf = 0;
+  size_t tb = 0, pm = 0, eg = 0, eb = 0, wf = 0, qf = 0, uf = 0, of = 0, fc = 0, kt = 0;
   if (wy) {
     wf = take(kWyWBytes * cc);
-    pf = take(kWyPBytes * cc);
+    qf = take(kWyQBytes * cc);
     uf = take(sizeof(float) * cc * p.C * p.d_v);
+    of = take(sizeof(float) * cc * p.C * p.d_v);
     fc = take(sizeof(float) * cc * kWyFac);
     kt = take(kWyKtBytes * (size_t)p.max_chunks * p.H_qk);
-    qf = take(kWyQBytes * (size_t)p.max_chunks * p.H_qk);
   } else {
     tb = take(sizeof(float) * cc * p.C * p.C);
     pm = take(sizeof(float) * cc * p.C * p.C);
@@ -951,11 +951,11 @@ Workspace workspace_layout(const Problem &p, bool states, void *base) {
     w.chunk_first = reinterpret_cast<int32_t *>(b + cf);
     if (wy) {
       w.wf = reinterpret_cast<unsigned char *>(b + wf);
-      w.pf = reinterpret_cast<unsigned char *>(b + pf);
+      w.qf = reinterpret_cast<unsigned char *>(b + qf);
       w.uf = reinterpret_cast<float *>(b + uf);
+      w.of = reinterpret_cast<float *>(b + of);
       w.fac = reinterpret_cast<float *>(b + fc);
       w.ktf = reinterpret_cast<unsigned char *>(b + kt);
-      w.qf = reinterpret_cast<unsigned char *>(b + qf);
     } else {
       w.tb = reinterpret_cast<float *>(b + tb);
       w.pm = reinterpret_cast<float *>(b + pm);

@@ -34,12 +34,12 @@ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 //   (the fp32 path keeps tb, pm, eg, eb; the bf16 path keeps instead, per
 //    (chunk, value head) slot, the operands of its state carry in MFMA
 //    fragment order -- see gdn_wy.hip)
-//   wf          bf16 [H_v, max_chunks, 32 KiB]   W = T diag(beta e^G) K, hi/lo
-//   pf          bf16 [H_v, max_chunks, 16 KiB]   P, hi/lo
+//   wf          f16  [H_v, max_chunks, 16 KiB]   W = T diag(beta e^G) K^
+//   qf          f16  [H_v, max_chunks, 16 KiB]   Q' = diag(e^G) Q^ - P W
 //   uf          f32  [H_v, max_chunks, C, d_v]   U' = T diag(beta) V
-//   fac         f32  [H_v, max_chunks, 160]      e^G q-norm, e^{G_last - G} k-norm, e^{G_last}
-//   ktf         bf16 [H_qk, max_chunks, 16 KiB]  K^T
-//   qf          bf16 [H_qk, max_chunks, 16 KiB]  Q
+//   of          f32  [H_v, max_chunks, C, d_v]   O' = P U'
+//   fac         f32  [H_v, max_chunks, 80]       e^{G_last - G}, e^{G_last}
+//   ktf         f16  [H_qk, max_chunks, 16 KiB]  K^^T (normalised keys)
 //   (states path only)
 //   u           f32 [T_tot, H_v, d_v]        per-token write vectors
 //   sc          f32 [max_chunks, H_v, d_k, d_v]  state at each chunk start
@@ -48,15 +48,15 @@ struct Workspace {
   int32_t *seq_start = nullptr;
   int32_t *chunk_first = nullptr;
   float *tb = nullptr, *pm = nullptr, *eg = nullptr, *eb = nullptr;
-  unsigned char *wf = nullptr, *pf = nullptr, *ktf = nullptr, *qf = nullptr;
-  float *uf = nullptr, *fac = nullptr;
+  unsigned char *wf = nullptr, *qf = nullptr, *ktf = nullptr;
+  float *uf = nullptr, *of = nullptr, *fac = nullptr;
   float *u = nullptr, *sc = nullptr;
   size_t bytes = 0;
 };
 
 // Per-slot sizes of the bf16 path's carry operands (d_k = 128, C = 64).
-constexpr size_t kWyWBytes = 32768, kWyPBytes = 16384, kWyKtBytes = 16384, kWyQBytes = 16384;
-constexpr int kWyFac = 160;
+constexpr size_t kWyWBytes = 16384, kWyQBytes = 16384, kWyKtBytes = 16384;
+constexpr int kWyFac = 80;
 
 // Computes the layout; with base == nullptr only `bytes` is meaningful.
 Workspace workspace_layout(const Problem &p, bool states, void *base);

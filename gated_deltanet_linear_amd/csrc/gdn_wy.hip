@@ -5,20 +5,24 @@
 // page, note "The DeltaNet mixer") in the UT / WY chunk form, arranged so that
 // the sequential part -- the carry of the state S from chunk to chunk -- holds
 // only the products that depend on S.  Per (chunk, value head), with the
-// in-chunk cumulative log decay G_r = g_0 + ... + g_r:
+// in-chunk cumulative log decay G_r = g_0 + ... + g_r, normalised keys
+// K^ = diag(rk) K and scaled queries Q^ = diag(rq) Q (rq = scale, times the
+// row's inverse norm with GDN_QK_L2NORM; rk = 1 or that norm):
 //
-//   A[r,i] = beta_r e^{G_r - G_i} (k_r . k_i), i < r       T = (I + A)^{-1}
-//   P[r,i] = e^{G_r - G_i} (q_r . k_i), i <= r
-//   W      = T diag(beta e^G) K        (C x d_k)       prep, all chunks at once
-//   U'     = T diag(beta) V            (C x d_v)       prep, all chunks at once
+//   A[r,i] = beta_r e^{G_r - G_i} (k^_r . k^_i), i < r      T = (I + A)^{-1}
+//   P[r,i] = e^{G_r - G_i} (q^_r . k^_i), i <= r            R = P T
+//   W      = T diag(beta e^G) K^          (C x d_k)  \
+//   U'     = T diag(beta) V               (C x d_v)   | prep, all chunks
+//   Q'     = diag(e^G) Q^ - R diag(beta e^G) K^         | at once
+//   O'     = R diag(beta) V                            /
 //   U      = U' - W S                                  chain
-//   O      = diag(e^G) Q S + P U                       chain
-//   S     <- e^{G_last} S + K^T diag(e^{G_last - G}) U chain
+//   O      = Q' S + O'                                 chain
+//   S     <- e^{G_last} S + K^^T diag(e^{G_last - G}) U chain
 //
-// U' - W S is T diag(beta) (V - diag(e^G) K S), the tokens' write vectors of
-// the token recursion.  With l2norm, k and q carry their row norms as factors
-// inside W, P and the per-token vectors, and K, Q themselves stay the exact
-// bf16 inputs.
+// U' - W S is T diag(beta) (V - diag(e^G) K^ S), the tokens' write vectors of
+// the token recursion, and Q' S + O' = diag(e^G) Q^ S + P U: the output's
+// intra-chunk part P U' is formed in prep at full precision, and the chain's
+// output needs S alone.
 //
 // Launch sequence: plan (gdn_chunk.hip), prep (chunk, value head), chain
 // (sequence, value head, block of 16 NB value columns), and on the states path
@@ -26,14 +30,14 @@
 //
 // Chain: 8 waves per block.  Waves 0-3 carry the state: wave w keeps rows
 // [32w, 32w + 32) of the S block in registers and forms U for the token tile
-// [16w, 16w + 16); waves 4-7 form O from the S and U that the state waves
-// publish in LDS (bf16 hi/lo): two barriers per chunk.  Every operand that does
-// not depend on S is loaded from the workspace straight into registers, one
-// chunk ahead, in the lane order of the MFMA that consumes it; nothing but S
-// and U passes through LDS.
+// [16w, 16w + 16); waves 4-7 form O from the S that the state waves publish in
+// LDS: two barriers per chunk.  Every operand that does not depend on S is
+// loaded from the workspace straight into registers, one chunk ahead, in the
+// lane order of the MFMA that consumes it; nothing but S and U passes through
+// LDS.
 //
-// MFMA lane order (v_mfma_f32_16x16x32_bf16): lane l feeds row l%16 of A and
-// column l%16 of B, and 8 contraction indices given by the group l/16.  The
+// MFMA lane order (v_mfma_f32_16x16x32_{bf16,f16}): lane l feeds row l%16 of A
+// and column l%16 of B, and 8 contraction indices given by the group l/16.  The
 // accumulator holds rows 4(l/16) + i, i < 4, of column l%16.  Here the 8
 // contraction indices of group g in step s are {32s + 4g + i, 32s + 16 + 4g + i},
 // i < 4: the rows that lane l holds in the accumulators of two vertically
@@ -41,8 +45,16 @@
 // without any transposition, and every workspace operand is stored in that
 // order.
 //
-// Precision: as on the fp32 path, products of computed values (S, W, U, P)
-// enter MFMA as bf16 hi/lo pairs (hi*hi + hi*lo + lo*hi); q, k, v enter once.
+// Precision.  Prep: q, k, v enter bf16 MFMA exactly; computed fp32 operands
+// (T, P, R and their diagonal scalings) enter as bf16 hi/lo pairs (hi*hi +
+// hi*lo + lo*hi).  Chain: its operands are fp16 (11 significant bits): W, Q'
+// and S once, K^ once (exact for the bf16 inputs in fp16's normal range), and
+// the write vectors diag(e^{G_last - G}) U as an fp16 hi/lo pair, which keeps
+// the state's own rounding at ~2^-22 per chunk.  A numpy emulation of this
+// placement on the 4096-token prefill laws gives max |dO| ~2e-3 x RMS(o) and a
+// final-state error ~1e-7 (6e-5 with slow decays), against single-fp16 P U
+// (6e-3 x RMS), which is why the P U' product stays in prep.  fp16's range
+// bounds the carried values: |S|, |W| and |Q'| entries must stay below 65504.
 #include <atomic>
 #include <type_traits>
 
@@ -60,28 +72,42 @@ constexpr int LDT = C + 2;   // K^T, V^T rows (bf16): an odd number of words spr
 constexpr int LDF = C + 4;   // fp32 C x C
 constexpr float kFloor = -1.0e4f;
 
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
 __device__ __forceinline__ bf16x8 ld8(const uint16_t *p) { return *reinterpret_cast<const bf16x8 *>(p); }
-// 8 bf16 from a 4-byte aligned LDS address.
-__device__ __forceinline__ bf16x8 ld8w(const uint16_t *p) {
+// bf16 elements p[0..3] and p[16..19] (4-byte aligned): the split contraction order.
+__device__ __forceinline__ bf16x8 ld8s(const uint16_t *p) {
   const uint32_t *q = reinterpret_cast<const uint32_t *>(p);
-  return __builtin_bit_cast(bf16x8, u32x4{q[0], q[1], q[2], q[3]});
+  return __builtin_bit_cast(bf16x8, u32x4{q[0], q[1], q[8], q[9]});
 }
 // e^x on the hardware exponential (v_exp_f32 of x log2 e): relative error a few
 // ulp for the decay arguments met here (|x| below a few hundred).
 __device__ __forceinline__ float fexp(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
 __device__ __forceinline__ bf16x8 as_bf(const u32x4 &x) { return __builtin_bit_cast(bf16x8, x); }
+__device__ __forceinline__ f16x8 as_h(const u32x4 &x) { return __builtin_bit_cast(f16x8, x); }
+__device__ __forceinline__ f32x4 mfma_f16(const u32x4 &a, const u32x4 &b, const f32x4 &c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(as_h(a), as_h(b), c, 0, 0, 0);
+}
 
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 // Two fp32 values -> one packed bf16 pair (v_cvt_pk_bf16_f32, round to nearest
 // even), and the pair's halves back as fp32.
 __device__ __forceinline__ uint32_t pk_bf16(float x, float y) {
-  typedef float f32x2_t __attribute__((ext_vector_type(2)));
   typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{x, y}, bf16x2_t));
 }
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
+// The same for fp16 (v_cvt_pk_f16_f32, round to nearest even).
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pk_f16(float x, float y) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{x, y}, f16x2_t));
+}
+__device__ __forceinline__ f32x2_t unpk_f16(uint32_t w) {
+  return __builtin_convertvector(__builtin_bit_cast(f16x2_t, w), f32x2_t);
+}
 
-// x = hi + lo + O(2^-17 |x|) for the 4 values of a.
+// x = hi + lo + O(2^-17 |x|) for the 4 values of a (bf16).
 __device__ __forceinline__ void split4(const f32x4 &a, u32x2 &hi, u32x2 &lo) {
   const uint32_t h0 = pk_bf16(a[0], a[1]), h1 = pk_bf16(a[2], a[3]);
   hi = u32x2{h0, h1};
@@ -95,17 +121,23 @@ __device__ __forceinline__ void split8(const f32x4 &a, const f32x4 &b, u32x4 &hi
   hi = u32x4{ah[0], ah[1], bh[0], bh[1]};
   lo = u32x4{al[0], al[1], bl[0], bl[1]};
 }
-__device__ __forceinline__ u32x4 cat(const u32x2 &a, const u32x2 &b) { return u32x4{a[0], a[1], b[0], b[1]}; }
-template <bool BF> __device__ __forceinline__ auto out_cvt(float x) {
-  if constexpr (BF) return f2bf(x);
-  else return x;
+// fp16: the 4 values of a once, and as hi + lo (x = hi + lo + O(2^-22 |x|) in
+// fp16's normal range).
+__device__ __forceinline__ u32x2 h16x4(const f32x4 &a) { return u32x2{pk_f16(a[0], a[1]), pk_f16(a[2], a[3])}; }
+__device__ __forceinline__ u32x4 h16x8(const f32x4 &a, const f32x4 &b) {
+  return u32x4{pk_f16(a[0], a[1]), pk_f16(a[2], a[3]), pk_f16(b[0], b[1]), pk_f16(b[2], b[3])};
+}
+__device__ __forceinline__ void split4h(const f32x4 &a, u32x2 &hi, u32x2 &lo) {
+  hi = h16x4(a);
+  const f32x2_t h0 = unpk_f16(hi[0]), h1 = unpk_f16(hi[1]);
+  lo = u32x2{pk_f16(a[0] - h0[0], a[1] - h0[1]), pk_f16(a[2] - h1[0], a[3] - h1[1])};
 }
 
 // ---------------------------------------------------------------------------
 // prep: one (chunk, value head) per block of 4 waves.  Wave w owns token tile
-// [16w, 16w + 16): its rows of P, W and U'.  One LDS region (36 KiB, four
-// blocks per CU) holds in turn the q, k rows, then A and T (fp32), then K^T and
-// V^T (bf16).
+// [16w, 16w + 16): its rows of P, R, W, U', Q' and O'.  One LDS region (36 KiB,
+// four blocks per CU) holds in turn the q, k rows, then A and T (fp32), then
+// K^T and V^T (bf16).
 // ---------------------------------------------------------------------------
 struct PrepSmem {
   static constexpr int RA = 2 * C * LDQ * 2, RB = 2 * C * LDF * 4, RC = (DK + 128) * LDT * 2;
@@ -118,17 +150,30 @@ struct PrepSmem {
 __global__ __launch_bounds__(256) void wy_prep_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
     const float *__restrict__ g, const float *__restrict__ beta, const Seqs seqs,
-    unsigned char *__restrict__ wf, unsigned char *__restrict__ pf, float *__restrict__ uf,
-    float *__restrict__ fac, unsigned char *__restrict__ ktf, unsigned char *__restrict__ qf, int H_qk,
-    int H_v, int d_v, int MC, float scale, int l2norm) {
+    unsigned char *__restrict__ wf, unsigned char *__restrict__ qf, float *__restrict__ uf,
+    float *__restrict__ of, float *__restrict__ fac, unsigned char *__restrict__ ktf, int H_qk, int H_v,
+    int d_v, int MC, float scale, int l2norm) {
   __shared__ PrepSmem sm;
   if (seqs.bad()) return;
-  const int c = blockIdx.x;
-  if (c >= seqs.chunks()) return;
+  // Chunks run last to first, so that the chain's first chunks are the ones
+  // written last (still in the Infinity Cache, and in L2 below); within a chunk,
+  // the value heads are ordered so that the block of head h lands on the XCD of
+  // the chain group that reads it (workgroups are dealt to the 8 XCDs round
+  // robin; the chain puts (sequence n, query/key head j) on XCD (n H_qk + j) % 8).
+  const int cpos = blockIdx.x / H_v, p = blockIdx.x % H_v;
+  const int nch = seqs.chunks();
+  if (cpos >= nch) return;
+  const int c = nch - 1 - cpos;
   const int n = seqs.seq_of(c);
   const int t0 = seqs.start(n) + (c - seqs.first(n)) * C;
   const int len = min(C, seqs.start(n + 1) - t0);
-  const int h = blockIdx.y, R = H_v / H_qk, j = h / R;
+  const int R = H_v / H_qk;
+  int h = p;
+  if (H_qk % 8 == 0 && H_v % 8 == 0) {
+    const int x = p & 7, kk = p >> 3;  // XCD of this block, and its rank among the chunk's blocks there
+    h = (x + 8 * (kk / R)) * R + kk % R;
+  }
+  const int j = h / R;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lr = lane & 15, lg = lane >> 4;
@@ -166,17 +211,6 @@ __global__ __launch_bounds__(256) void wy_prep_kernel(
     sm.beta[lane] = lane < len ? braw : 0.f;
   }
   __syncthreads();
-  // Q fragments, once per (chunk, query/key head): item (token tile w, d_k step
-  // s, lane) = Q[16w + l%16][{32s + 4g + i, 32s + 16 + 4g + i}].
-  if (h % R == 0) {
-    u32x4 *Q4 = reinterpret_cast<u32x4 *>(qf + ((int64_t)j * MC + c) * kWyQBytes);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int it = tid + 256 * i, ln = it & 63, ws = it >> 6;
-      const uint16_t *row = sq + (16 * (ws >> 2) + (ln & 15)) * LDQ + 32 * (ws & 3) + 4 * (ln >> 4);
-      Q4[it] = cat(*reinterpret_cast<const u32x2 *>(row), *reinterpret_cast<const u32x2 *>(row + 16));
-    }
-  }
   if (tid < 2 * C) {
     const int r = tid % C;
     float rn = 1.f;
@@ -194,7 +228,8 @@ __global__ __launch_bounds__(256) void wy_prep_kernel(
   }
   // Gram tiles, 5 per wave, kept in registers: wave w takes the w + 1 tiles
   // (K Q^T)[16 ni.., 16 w..], ni <= w, whose accumulators hold P's rows of token
-  // tile w in the carry's lane order, and 4 - w of the 10 lower tiles of K K^T.
+  // tile w (lane: row 16w + l%16, columns 16 ni + 4(l/16) + i), and 4 - w of the
+  // 10 lower tiles of K K^T.
   constexpr int kKKFirst[4] = {0, 4, 7, 9};
   f32x4 acc[5];
   int kmi[5], kni[5];
@@ -221,27 +256,15 @@ __global__ __launch_bounds__(256) void wy_prep_kernel(
 
   float *A = reinterpret_cast<float *>(sm.r), *Tm = A + C * LDF;
   {
-    u32x4 *P4 = reinterpret_cast<u32x4 *>(pf + slot * kWyPBytes);
     const int r = 16 * w + lr;  // P row of this lane
 #pragma unroll
     for (int m = 0; m < 5; ++m) {
       if (m <= w) {
-        // P[r][16m + 4lg + i] = rq_r rk_i e^{G_r - G_i} (q_r . k_i), i <= r
-        f32x4 pv;
+        // P[r][16m + 4lg + i] = rq_r rk_i e^{G_r - G_i} (q_r . k_i), i <= r; kept in acc[m]
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int ci = 16 * m + 4 * lg + e;
-          pv[e] = ci <= r ? sm.rq[r] * sm.rk[ci] * fexp((float)(sm.gam[r] - sm.gam[ci])) * acc[m][e] : 0.f;
-        }
-        u32x2 hi, lo;
-        split4(pv, hi, lo);
-        // fragment (w, st = m / 2): elements 0-3 from tile 2st, 4-7 from tile 2st + 1
-        u32x2 *P2 = reinterpret_cast<u32x2 *>(P4 + ((w * 2 + (m >> 1)) * 2) * 64 + lane) + (m & 1);
-        P2[0] = hi;
-        P2[128] = lo;  // the lo plane is 64 lanes (1 KiB) further
-        if ((m & 1) == 0 && m == w) {  // tile 2st + 1 is above the diagonal: zero
-          P2[1] = u32x2{0u, 0u};
-          P2[129] = u32x2{0u, 0u};
+          acc[m][e] = ci <= r ? sm.rq[r] * sm.rk[ci] * fexp((float)(sm.gam[r] - sm.gam[ci])) * acc[m][e] : 0.f;
         }
       } else {
         // A[r][i] = beta_r rk_r rk_i e^{G_r - G_i} (k_r . k_i), i < r
@@ -256,13 +279,12 @@ __global__ __launch_bounds__(256) void wy_prep_kernel(
       }
     }
   }
-  // Per-token factors: e^G q-norm (scale included), e^{G_last - G} k-norm, e^{G_last}.
+  // Per-token factors of the carry: e^{G_last - G} (zero past the length), e^{G_last}.
   if (tid < C) {
     float *F = fac + slot * kWyFac;
     const double gl = sm.gam[len - 1];
-    F[tid] = sm.eg[tid] * sm.rq[tid];
-    F[C + tid] = tid < len ? fexp((float)(gl - sm.gam[tid])) * sm.rk[tid] : 0.f;
-    if (tid == 0) F[2 * C] = fexp((float)gl);
+    F[tid] = tid < len ? fexp((float)(gl - sm.gam[tid])) : 0.f;
+    if (tid == 0) F[C] = fexp((float)gl);
   }
   __syncthreads();
 
@@ -287,7 +309,8 @@ __global__ __launch_bounds__(256) void wy_prep_kernel(
   //   T_ib,jb = -T_ib,ib * Y,  Y = sum_{m=jb}^{ib-1} A_ib,m T_m,jb     (fp32 MFMA 16x16x4)
   // Y's MFMA feeds contraction index 4s + l/16 in step s; the second product
   // feeds 4(l/16) + s, which makes its B operand in step s this lane's own
-  // accumulator element Y[4(l/16) + s][l%16].
+  // accumulator element Y[4(l/16) + s][l%16].  Blocks above the diagonal are
+  // never written: every reader below masks them.
   if (w < 3) {
     const int jb = w;
     for (int ib = jb + 1; ib < 4; ++ib) {
@@ -306,30 +329,56 @@ __global__ __launch_bounds__(256) void wy_prep_kernel(
   }
   __syncthreads();
 
-  // This wave's fragments of T' = T diag(beta e^G k-norm) and T'' = T diag(beta)
-  // (rows of token tile w, columns 32 st + 8 lg .. + 7), bf16 hi/lo.  T' is the
-  // B operand of W^T = K^T T'^T and T'' the A operand of U' = T'' V.
-  u32x4 t1h[2], t1l[2], t2h[2], t2l[2];
+  // This lane's row of T (row 16w + l%16, token step st in the split order
+  // {32 st + 4g + i, 32 st + 16 + 4g + i}; zero above the diagonal), kept in
+  // registers across the barrier that retires T.
+  const int rw = 16 * w + lr;
+  f32x4 ta[2], tb[2];
 #pragma unroll
   for (int st = 0; st < 2; ++st) {
+    ta[st] = tb[st] = f32x4{0.f, 0.f, 0.f, 0.f};
     if (st <= (w >> 1)) {
-      const int r = 16 * w + lr;
-      f32x4 a1, b1, a2, b2;
+      const int i0 = 32 * st + 4 * lg;
+      const f32x4 x0 = *reinterpret_cast<const f32x4 *>(Tm + rw * LDF + i0);
+      const f32x4 x1 = *reinterpret_cast<const f32x4 *>(Tm + rw * LDF + i0 + 16);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int ci = 32 * st + 8 * lg + e;
-        const float t = ci <= r ? Tm[r * LDF + ci] * sm.beta[ci] : 0.f;
-        const float t1 = t * sm.eg[ci] * sm.rk[ci];
-        if (e < 4) {
-          a2[e] = t;
-          a1[e] = t1;
-        } else {
-          b2[e - 4] = t;
-          b1[e - 4] = t1;
+      for (int e = 0; e < 4; ++e) {
+        ta[st][e] = i0 + e <= rw ? x0[e] : 0.f;
+        tb[st][e] = i0 + 16 + e <= rw ? x1[e] : 0.f;
+      }
+    }
+  }
+  // R = P T for the rows of token tile w, as the tiles nt <= w of R^T = T^T P^T
+  // (contraction over tokens in the split order).  The B operand P^T is this
+  // lane's own P accumulators: P[16w + l%16][32 st + 4g + i] = acc[2st][i] and
+  // [.. + 16] = acc[2st + 1][i].  racc[nt][i] = R[16w + l%16][16 nt + 4g + i].
+  f32x4 racc[4];
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) racc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int st = 0; st < 2; ++st) {
+    if (2 * st <= w) {
+      const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+      u32x4 ph, pl;
+      split8(acc[2 * st], 2 * st + 1 <= w ? acc[2 * st + 1] : z4, ph, pl);
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        if (nt <= w && nt <= 2 * st + 1) {
+          const int nn = 16 * nt + lr;
+          f32x4 xa, xb;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int i0 = 32 * st + 4 * lg + e, i1 = i0 + 16;
+            xa[e] = i0 >= nn ? Tm[i0 * LDF + nn] : 0.f;  // T is lower triangular
+            xb[e] = i1 >= nn ? Tm[i1 * LDF + nn] : 0.f;
+          }
+          u32x4 th, tl;
+          split8(xa, xb, th, tl);
+          racc[nt] = mfma_bf16(as_bf(th), as_bf(ph), racc[nt]);
+          racc[nt] = mfma_bf16(as_bf(th), as_bf(pl), racc[nt]);
+          racc[nt] = mfma_bf16(as_bf(tl), as_bf(ph), racc[nt]);
         }
       }
-      split8(a1, b1, t1h[st], t1l[st]);
-      split8(a2, b2, t2h[st], t2l[st]);
     }
   }
   __syncthreads();  // A and T are dead; the region holds K^T and V^T from here
@@ -347,58 +396,120 @@ __global__ __launch_bounds__(256) void wy_prep_kernel(
       for (int e = 0; e < 8; ++e) vt[(cvv * 8 + e) * LDT + rv] = (uint16_t)(c4[e >> 1] >> (16 * (e & 1)));
     }
   }
-  __syncthreads();
-
-  // W^T = K^T T'^T for token tile w, by d_k step s: the tiles of d_k rows 32s..
-  // and 32s+16.. give this lane W[16w + l%16][{32s + 4g + i, 32s + 16 + 4g + i}].
+  // This lane's query row for Q' (row 16w + l%16, d_k {32s + 4g + i, 32s + 16 + 4g + i}),
+  // read again from global memory (the chunk's rows are in L2).
+  u32x2 qa[4], qb[4];
   {
-    u32x4 *W4 = reinterpret_cast<u32x4 *>(wf + slot * kWyWBytes) + w * 8 * 64 + lane;
+    const uint16_t *qrow = q + ((int64_t)(t0 + min(rw, len - 1)) * H_qk + j) * DK + 4 * lg;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
+      qa[s] = *reinterpret_cast<const u32x2 *>(qrow + 32 * s);
+      qb[s] = *reinterpret_cast<const u32x2 *>(qrow + 32 * s + 16);
+    }
+  }
+  __syncthreads();
+
+  // Row fragments (token tile w, token step st, split order), bf16 hi/lo, with
+  // the column scalings of the four products below:
+  //   diag(beta e^G k-norm): T' for W, R' for Q';   diag(beta): T'' for U', R'' for O'.
+  auto frag = [&](const f32x4 &xa, const f32x4 &xb, int st, bool dk, u32x4 &hi, u32x4 &lo) {
+    f32x4 ya, yb;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int i0 = 32 * st + 4 * lg + e, i1 = i0 + 16;
+      ya[e] = xa[e] * sm.beta[i0] * (dk ? sm.eg[i0] * sm.rk[i0] : 1.f);
+      yb[e] = xb[e] * sm.beta[i1] * (dk ? sm.eg[i1] * sm.rk[i1] : 1.f);
+    }
+    split8(ya, yb, hi, lo);
+  };
+  // W^T = K^T T'^T and (R' K)^T = K^T R'^T for token tile w, by d_k step s: the
+  // tiles of d_k rows 32s.. and 32s+16.. give this lane row 16w + l%16 at d_k
+  // {32s + 4g + i, 32s + 16 + 4g + i}, the chain's A-operand order.  Both are
+  // stored as fp16; Q' = e^G q-norm scale Q - R' K.
+  {
+    u32x4 t1h[2], t1l[2], r1h[2], r1l[2];
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      if (st <= (w >> 1)) {
+        frag(ta[st], tb[st], st, true, t1h[st], t1l[st]);
+        frag(racc[2 * st], racc[2 * st + 1], st, true, r1h[st], r1l[st]);
+      }
+    }
+    u32x4 *W4 = reinterpret_cast<u32x4 *>(wf + slot * kWyWBytes) + w * 4 * 64 + lane;
+    u32x4 *Q4 = reinterpret_cast<u32x4 *>(qf + slot * kWyQBytes) + w * 4 * 64 + lane;
+    const float fq = sm.eg[rw] * sm.rq[rw];
+    const bool live = rw < len;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0, x0 = acc0, x1 = acc0;
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
-        if (st <= (w >> 1)) {  // T' is lower triangular
-          const int ko = 32 * st + 8 * lg;
-          const bf16x8 a0 = ld8w(kt + (32 * s + lr) * LDT + ko), a1 = ld8w(kt + (32 * s + 16 + lr) * LDT + ko);
+        if (st <= (w >> 1)) {  // T' and R' are lower triangular
+          const bf16x8 a0 = ld8s(kt + (32 * s + lr) * LDT + 32 * st + 4 * lg);
+          const bf16x8 a1 = ld8s(kt + (32 * s + 16 + lr) * LDT + 32 * st + 4 * lg);
           acc0 = mfma_bf16(a0, as_bf(t1h[st]), acc0);
           acc0 = mfma_bf16(a0, as_bf(t1l[st]), acc0);
           acc1 = mfma_bf16(a1, as_bf(t1h[st]), acc1);
           acc1 = mfma_bf16(a1, as_bf(t1l[st]), acc1);
+          x0 = mfma_bf16(a0, as_bf(r1h[st]), x0);
+          x0 = mfma_bf16(a0, as_bf(r1l[st]), x0);
+          x1 = mfma_bf16(a1, as_bf(r1h[st]), x1);
+          x1 = mfma_bf16(a1, as_bf(r1l[st]), x1);
         }
       }
-      u32x4 hi, lo;
-      split8(acc0, acc1, hi, lo);
-      W4[(s * 2 + 0) * 64] = hi;
-      W4[(s * 2 + 1) * 64] = lo;
+      W4[s * 64] = h16x8(acc0, acc1);
+      f32x4 y0, y1;
+      y0[0] = bf_lo(qa[s][0]); y0[1] = bf_hi(qa[s][0]); y0[2] = bf_lo(qa[s][1]); y0[3] = bf_hi(qa[s][1]);
+      y1[0] = bf_lo(qb[s][0]); y1[1] = bf_hi(qb[s][0]); y1[2] = bf_lo(qb[s][1]); y1[3] = bf_hi(qb[s][1]);
+      const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+      Q4[s * 64] = h16x8(live ? y0 * fq - x0 : z4, live ? y1 * fq - x1 : z4);
     }
   }
-  // U' = T'' V for token tile w, by value column tile ct, in accumulator order.
+  // U' = T'' V and O' = R'' V for token tile w, by value column tile ct, in
+  // accumulator order (fp32).
   {
+    u32x4 t2h[2], t2l[2], r2h[2], r2l[2];
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      if (st <= (w >> 1)) {
+        frag(ta[st], tb[st], st, false, t2h[st], t2l[st]);
+        frag(racc[2 * st], racc[2 * st + 1], st, false, r2h[st], r2l[st]);
+      }
+    }
     const int NCT = d_v / 16;
     f32x4 *U4 = reinterpret_cast<f32x4 *>(uf + slot * (int64_t)(C * d_v)) + w * NCT * 64 + lane;
+    f32x4 *O4 = reinterpret_cast<f32x4 *>(of + slot * (int64_t)(C * d_v)) + w * NCT * 64 + lane;
     for (int ct = 0; ct < NCT; ++ct) {
-      f32x4 a = {0.f, 0.f, 0.f, 0.f};
+      f32x4 a = {0.f, 0.f, 0.f, 0.f}, b = a;
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
         if (st <= (w >> 1)) {
-          const bf16x8 b = ld8w(vt + (16 * ct + lr) * LDT + 32 * st + 8 * lg);
-          a = mfma_bf16(as_bf(t2h[st]), b, a);
-          a = mfma_bf16(as_bf(t2l[st]), b, a);
+          const bf16x8 bs = ld8s(vt + (16 * ct + lr) * LDT + 32 * st + 4 * lg);
+          a = mfma_bf16(as_bf(t2h[st]), bs, a);
+          a = mfma_bf16(as_bf(t2l[st]), bs, a);
+          b = mfma_bf16(as_bf(r2h[st]), bs, b);
+          b = mfma_bf16(as_bf(r2l[st]), bs, b);
         }
       }
       U4[ct * 64] = a;
+      O4[ct * 64] = b;
     }
   }
-  // K^T fragments, once per (chunk, query/key head): item (d_k tile mt, token
-  // step st, lane) = K^T[16 mt + l%16][{32 st + 4g + i, 32 st + 16 + 4g + i}].
+  // K^^T fragments (fp16, normalised keys), once per (chunk, query/key head):
+  // item (d_k tile mt, token step st, lane) = K^^T[16 mt + l%16][{32 st + 4g + i,
+  // 32 st + 16 + 4g + i}].
   if (h % R == 0) {
     u32x4 *K4 = reinterpret_cast<u32x4 *>(ktf + ((int64_t)j * MC + c) * kWyKtBytes);
     for (int it = tid; it < 16 * 64; it += 256) {
       const int ln = it & 63, ms = it >> 6, mt = ms >> 1, st = ms & 1;
-      const uint16_t *row = kt + (16 * mt + (ln & 15)) * LDT + 32 * st + 4 * (ln >> 4);
-      const uint32_t *r32 = reinterpret_cast<const uint32_t *>(row);
-      K4[it] = u32x4{r32[0], r32[1], r32[8], r32[9]};
+      const int t = 32 * st + 4 * (ln >> 4);
+      const uint32_t *r32 = reinterpret_cast<const uint32_t *>(kt + (16 * mt + (ln & 15)) * LDT + t);
+      f32x4 a, b;
+      a[0] = bf_lo(r32[0]) * sm.rk[t];      a[1] = bf_hi(r32[0]) * sm.rk[t + 1];
+      a[2] = bf_lo(r32[1]) * sm.rk[t + 2];  a[3] = bf_hi(r32[1]) * sm.rk[t + 3];
+      b[0] = bf_lo(r32[8]) * sm.rk[t + 16]; b[1] = bf_hi(r32[8]) * sm.rk[t + 17];
+      b[2] = bf_lo(r32[9]) * sm.rk[t + 18]; b[3] = bf_hi(r32[9]) * sm.rk[t + 19];
+      K4[it] = h16x8(a, b);
     }
   }
 }
@@ -408,60 +519,54 @@ __global__ __launch_bounds__(256) void wy_prep_kernel(
 // 8 waves.  Waves 0-3 carry the state: wave w keeps rows [32w, 32w + 32) of
 // the S block in registers and forms the write vectors U of token tile [16w,
 // 16w + 16).  Waves 4-7 produce the output: wave 4 + w computes O for token
-// tile w from the published S and U.  Per chunk c:
+// tile w from the published S.  Per chunk c:
 //
 //   state waves                          output waves
-//   publish S (bf16 hi/lo) -> sx[c&1]
+//   publish S (fp16) -> sx
 //   ---------------------------- barrier 1 ----------------------------
-//   U = U' - W S, U'' -> ux[c&1], u2x
+//   U = U' - W S, U'' -> u2x (hi/lo)     O = Q' S + O' (from sx), store O
 //   ---------------------------- barrier 2 ----------------------------
-//   S <- e^{G_last} S + K^T U''           O = e^G q-norm (Q S) + P U
-//                                          (from sx[c&1], ux[c&1])
+//   S <- e^{G_last} S + K^^T U''
 //
-// sx and ux are double-buffered by chunk parity, so the output waves work on
-// chunk c while the state waves already publish chunk c + 1; u2x is rewritten
-// only after every wave has passed the next barrier.  Every operand that does
-// not depend on S is loaded from the workspace straight into registers, one
-// chunk ahead, each group right after its last use, interleaved with the MFMAs
-// of its phase.
+// Every wave is done with sx and u2x of chunk c once it has passed the barrier
+// after its last read, so one buffer of each suffices.  Every operand that does
+// not depend on S is loaded from the workspace straight into registers ahead of
+// its use (the state waves' one chunk ahead, each group right after its last
+// use, interleaved with the MFMAs of its phase).
 //
 // NB = 1 gives the most blocks (the latency of one long sequence is spread over
 // every CU); NB = 2 halves the operand loads per column of S, for launches that
 // fill the GPU with blocks either way (many sequences, or many heads).
 // ---------------------------------------------------------------------------
 template <int NB> struct StateOps {
-  u32x4 w[4][2];   // W hi/lo of token tile w, d_k steps 0..3
-  u32x4 kt[2][2];  // K^T of this wave's two d_k tiles, token steps 0..1
+  u32x4 w[4];      // W (fp16) of token tile w, d_k steps 0..3
+  u32x4 kt[2][2];  // K^^T (fp16) of this wave's two d_k tiles, token steps 0..1
   f32x4 u[NB];     // U' tiles
-  f32x4 fu;        // e^{G_last - G} k-norm of this lane's 4 rows
+  f32x4 fu;        // e^{G_last - G} of this lane's 4 rows
   float el;        // e^{G_last}
 };
-struct OutOps {
-  u32x4 q[4];      // Q of token tile w, d_k steps 0..3
-  u32x4 p[2][2];   // P hi/lo of token tile w, token steps 0..1
-  f32x4 fq;        // e^G q-norm of this lane's 4 rows
+template <int NB> struct OutOps {
+  u32x4 q[4];      // Q' (fp16) of token tile w, d_k steps 0..3
+  f32x4 o[NB];     // O' tiles
 };
 
 template <bool STATES, bool OBF16, int NB>
 __global__ __launch_bounds__(512) void wy_chain_kernel(
     const float *__restrict__ s0, const Seqs sq, const unsigned char *__restrict__ wf,
-    const unsigned char *__restrict__ pf, const float *__restrict__ uf, const float *__restrict__ fac,
-    const unsigned char *__restrict__ ktf, const unsigned char *__restrict__ qf, void *__restrict__ o,
-    float *__restrict__ fin, float *__restrict__ uw, float *__restrict__ scw, int H_qk, int H_v,
-    int d_v, int MC, int groups) {
-  // S and U as published by their owner wave, in the owner's lane order, one
-  // 16-column tile nb after the other.  ux and u2x: the two token tiles of
-  // token step st side by side, so a reader takes its 8 contraction indices
-  // with one 16-byte load.
-  __shared__ u32x4 sx[2][4][NB][2][64];
-  __shared__ u32x4 ux[2][NB][2][2][64];
+    const unsigned char *__restrict__ qf, const float *__restrict__ uf, const float *__restrict__ of,
+    const float *__restrict__ fac, const unsigned char *__restrict__ ktf, void *__restrict__ o,
+    float *__restrict__ fin, float *__restrict__ uw, float *__restrict__ scw, int H_qk, int H_v, int d_v,
+    int MC, int groups) {
+  // S as published by its owner wave (the B operand of d_k step w), one
+  // 16-column tile nb after the other.  u2x: the two token tiles of token step
+  // st side by side, so a reader takes its 8 contraction indices with one
+  // 16-byte load.
+  __shared__ u32x4 sx[4][NB][64];
   __shared__ u32x4 u2x[NB][2][2][64];
-  constexpr int LDO = 20;  // O tile rows, fp32 (the pad spreads rows over the banks)
-  __shared__ float ot[4][16 * LDO];
   if (sq.bad()) return;
   const int NCT = d_v / 16;         // 16-column tiles of S
   const int NCB = NCT / NB;         // column blocks
-  // groups: (sequence, query/key head), whose value heads share K^T and Q too
+  // groups: (sequence, query/key head), whose value heads share K^T too
   const int u = xcd_group_remap(blockIdx.x, NCB * (H_v / H_qk), groups);
   if (u < 0) return;
   const int jb = u % NCB, h = (u / NCB) % H_v, n = u / (NCB * H_v);
@@ -497,7 +602,7 @@ __global__ __launch_bounds__(512) void wy_chain_kernel(
     __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
 
     auto wp = [&](int c) {
-      return reinterpret_cast<const u32x4 *>(wf + (hslot + c) * kWyWBytes) + w * 8 * 64 + lane;
+      return reinterpret_cast<const u32x4 *>(wf + (hslot + c) * kWyWBytes) + w * 4 * 64 + lane;
     };
     auto kp = [&](int c) {
       return reinterpret_cast<const u32x4 *>(ktf + (jslot + c) * kWyKtBytes) + 2 * w * 2 * 64 + lane;
@@ -507,8 +612,8 @@ __global__ __launch_bounds__(512) void wy_chain_kernel(
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) op.u[nb] = U4[(w * NCT + jb * NB + nb) * 64 + lane];
       const float *F = fac + (hslot + c) * kWyFac;
-      op.fu = *reinterpret_cast<const f32x4 *>(F + C + 16 * w + 4 * lg);
-      op.el = F[2 * C];
+      op.fu = *reinterpret_cast<const f32x4 *>(F + 16 * w + 4 * lg);
+      op.el = F[C];
     };
 
     auto chunk = [&](StateOps<NB> &op, int c, int cn) {
@@ -517,10 +622,7 @@ __global__ __launch_bounds__(512) void wy_chain_kernel(
       // 1. publish this wave's S rows (the B operand of d_k step w)
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
-        u32x4 hi, lo;
-        split8(S[nb][0], S[nb][1], hi, lo);
-        sx[c & 1][w][nb][0][lane] = hi;
-        sx[c & 1][w][nb][1][lane] = lo;
+        sx[w][nb][lane] = h16x8(S[nb][0], S[nb][1]);
         if constexpr (STATES) {
 #pragma unroll
           for (int mt = 0; mt < 2; ++mt)
@@ -531,39 +633,31 @@ __global__ __launch_bounds__(512) void wy_chain_kernel(
         }
       }
       __syncthreads();  // 1
-      // 2. U = U' - W S for token tile w (three accumulators: hi*hi, hi*lo, lo*hi)
+      // 2. U = U' - W S for token tile w (two accumulators: even and odd d_k steps)
       const u32x4 *W4 = wp(cn);
-      f32x4 a0[NB], a1[NB], a2[NB];
+      f32x4 a0[NB], a1[NB];
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) a0[nb] = a1[nb] = a2[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int nb = 0; nb < NB; ++nb) a0[nb] = a1[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
-          const bf16x8 sh = as_bf(sx[c & 1][s][nb][0][lane]), sl = as_bf(sx[c & 1][s][nb][1][lane]);
-          a0[nb] = mfma_bf16(as_bf(op.w[s][0]), sh, a0[nb]);
-          a1[nb] = mfma_bf16(as_bf(op.w[s][0]), sl, a1[nb]);
-          a2[nb] = mfma_bf16(as_bf(op.w[s][1]), sh, a2[nb]);
+          const u32x4 sv = sx[s][nb][lane];
+          if (s & 1) a1[nb] = mfma_f16(op.w[s], sv, a1[nb]);
+          else a0[nb] = mfma_f16(op.w[s], sv, a0[nb]);
         }
-        op.w[s][0] = W4[(s * 2 + 0) * 64];
-        op.w[s][1] = W4[(s * 2 + 1) * 64];
-        __builtin_amdgcn_sched_group_barrier(kDSR, 2 * NB, 0);
+        op.w[s] = W4[s * 64];
+        __builtin_amdgcn_sched_group_barrier(kDSR, NB, 0);
         __builtin_amdgcn_sched_group_barrier(kMFMA, NB, 0);
         __builtin_amdgcn_sched_group_barrier(kVMR, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(kMFMA, NB, 0);
-        __builtin_amdgcn_sched_group_barrier(kVMR, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(kMFMA, NB, 0);
       }
-      //    U'' = diag(e^{G_last - G} k-norm) U; publish U and U''
+      //    U'' = diag(e^{G_last - G}) U; publish U'' (fp16 hi/lo)
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
-        const f32x4 uv = op.u[nb] - (a0[nb] + a1[nb] + a2[nb]);
+        const f32x4 uv = op.u[nb] - (a0[nb] + a1[nb]);
         const f32x4 u2 = uv * op.fu;
         u32x2 hi, lo;
-        split4(uv, hi, lo);
-        reinterpret_cast<u32x2 *>(&ux[c & 1][nb][w >> 1][0][lane])[w & 1] = hi;
-        reinterpret_cast<u32x2 *>(&ux[c & 1][nb][w >> 1][1][lane])[w & 1] = lo;
-        split4(u2, hi, lo);
+        split4h(u2, hi, lo);
         reinterpret_cast<u32x2 *>(&u2x[nb][w >> 1][0][lane])[w & 1] = hi;
         reinterpret_cast<u32x2 *>(&u2x[nb][w >> 1][1][lane])[w & 1] = lo;
         if constexpr (STATES) {
@@ -577,17 +671,17 @@ __global__ __launch_bounds__(512) void wy_chain_kernel(
       const float el = op.el;
       load_uf(op, cn);
       __syncthreads();  // 2
-      // 3. S <- e^{G_last} S + K^T U'' for this wave's rows
-      bf16x8 bh[NB][2], bl[NB][2];
+      // 3. S <- e^{G_last} S + K^^T U'' for this wave's rows
+      u32x4 bh[NB][2], bl[NB][2];
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
         for (int st = 0; st < 2; ++st) {
-          bh[nb][st] = as_bf(u2x[nb][st][0][lane]);
-          bl[nb][st] = as_bf(u2x[nb][st][1][lane]);
+          bh[nb][st] = u2x[nb][st][0][lane];
+          bl[nb][st] = u2x[nb][st][1][lane];
         }
       const u32x4 *K4 = kp(cn);
-      f32x4 ah[NB][2], al[NB][2];  // K^T U''_hi and K^T U''_lo: independent chains
+      f32x4 ah[NB][2], al[NB][2];  // K^^T U''_hi and K^^T U''_lo: independent chains
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt) {
 #pragma unroll
@@ -596,8 +690,8 @@ __global__ __launch_bounds__(512) void wy_chain_kernel(
         for (int st = 0; st < 2; ++st) {
 #pragma unroll
           for (int nb = 0; nb < NB; ++nb) {
-            ah[nb][mt] = mfma_bf16(as_bf(op.kt[mt][st]), bh[nb][st], ah[nb][mt]);
-            al[nb][mt] = mfma_bf16(as_bf(op.kt[mt][st]), bl[nb][st], al[nb][mt]);
+            ah[nb][mt] = mfma_f16(op.kt[mt][st], bh[nb][st], ah[nb][mt]);
+            al[nb][mt] = mfma_f16(op.kt[mt][st], bl[nb][st], al[nb][mt]);
           }
           op.kt[mt][st] = K4[(mt * 2 + st) * 64];
         }
@@ -619,10 +713,7 @@ __global__ __launch_bounds__(512) void wy_chain_kernel(
       {
         const u32x4 *W4 = wp(c_begin), *K4 = kp(c_begin);
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          op.w[s][0] = W4[(s * 2 + 0) * 64];
-          op.w[s][1] = W4[(s * 2 + 1) * 64];
-        }
+        for (int s = 0; s < 4; ++s) op.w[s] = W4[s * 64];
         load_uf(op, c_begin);
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
@@ -646,93 +737,70 @@ __global__ __launch_bounds__(512) void wy_chain_kernel(
     }
   } else {
     // ------------------------------ output waves -----------------------------
-    auto qp = [&](int c) { return reinterpret_cast<const u32x4 *>(qf + (jslot + c) * kWyQBytes) + w * 4 * 64 + lane; };
-    auto pp = [&](int c) { return reinterpret_cast<const u32x4 *>(pf + (hslot + c) * kWyPBytes) + w * 2 * 2 * 64 + lane; };
-    auto fq_of = [&](int c) { return *reinterpret_cast<const f32x4 *>(fac + (hslot + c) * kWyFac + 16 * w + 4 * lg); };
-    auto load_p = [&](OutOps &op, int c) {
-      const u32x4 *P4 = pp(c);
+    // O for chunk c is formed between the chunk's two barriers, while the state
+    // waves form U (the output needs S alone), and stored directly: lane l holds
+    // rows 4(l/16) + i of column l%16, so each store covers 4 rows x 64 bytes,
+    // the same 64-byte row segments a transposed store would write.  Operands
+    // are loaded two chunks ahead, in two register sets used alternately.
+    auto qp = [&](int c) {
+      return reinterpret_cast<const u32x4 *>(qf + (hslot + c) * kWyQBytes) + w * 4 * 64 + lane;
+    };
+    auto load_out = [&](OutOps<NB> &op, int c) {
+      const u32x4 *Q4 = qp(c);
 #pragma unroll
-      for (int st = 0; st < 2; ++st)
-        if (st <= (w >> 1))  // P is lower triangular: token tiles 0, 1 use step 0 only
+      for (int s = 0; s < 4; ++s) op.q[s] = Q4[s * 64];
+      const f32x4 *O4 = reinterpret_cast<const f32x4 *>(of + (hslot + c) * (int64_t)(C * d_v));
 #pragma unroll
-          for (int pl = 0; pl < 2; ++pl) op.p[st][pl] = P4[(st * 2 + pl) * 64];
+      for (int nb = 0; nb < NB; ++nb) op.o[nb] = O4[(w * NCT + jb * NB + nb) * 64 + lane];
     };
 
-    auto chunk = [&](OutOps &op, int c, int cn) {
+    auto chunk = [&](OutOps<NB> &op, int c, int cn) {
       const int t0 = s_begin + (c - c_begin) * C;
       const int len = min(C, s_end - t0);
       __syncthreads();  // 1
-      __syncthreads();  // 2
-      // Q S for token tile w, from the S published for this chunk
-      f32x4 aq[NB], aq2[NB];
+      // O = Q' S + O' for token tile w, from the S published for this chunk
+      f32x4 ao[NB], ao2[NB];
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) aq[nb] = aq2[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int nb = 0; nb < NB; ++nb) {
+        ao[nb] = op.o[nb];
+        ao2[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
 #pragma unroll
       for (int s = 0; s < 4; ++s)
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
-          const bf16x8 sh = as_bf(sx[c & 1][s][nb][0][lane]), sl = as_bf(sx[c & 1][s][nb][1][lane]);
-          aq[nb] = mfma_bf16(as_bf(op.q[s]), sh, aq[nb]);
-          aq2[nb] = mfma_bf16(as_bf(op.q[s]), sl, aq2[nb]);
+          const u32x4 sv = sx[s][nb][lane];
+          if (s & 1) ao2[nb] = mfma_f16(op.q[s], sv, ao2[nb]);
+          else ao[nb] = mfma_f16(op.q[s], sv, ao[nb]);
         }
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) aq[nb] = (aq[nb] + aq2[nb]) * op.fq;
-      // O = e^G q-norm (Q S) + P U for token tile w
-#pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        if (st <= (w >> 1)) {
-#pragma unroll
-          for (int nb = 0; nb < NB; ++nb) {
-            const bf16x8 bh = as_bf(ux[c & 1][nb][st][0][lane]), bl = as_bf(ux[c & 1][nb][st][1][lane]);
-            aq[nb] = mfma_bf16(as_bf(op.p[st][0]), bh, aq[nb]);
-            aq[nb] = mfma_bf16(as_bf(op.p[st][0]), bl, aq[nb]);
-            aq[nb] = mfma_bf16(as_bf(op.p[st][1]), bh, aq[nb]);
-          }
-        }
-      }
-      // the next chunk's operands
-      {
-        const u32x4 *Q4 = qp(cn);
-#pragma unroll
-        for (int s = 0; s < 4; ++s) op.q[s] = Q4[s * 64];
-        op.fq = fq_of(cn);
-        load_p(op, cn);
-      }
+      load_out(op, cn);
       if (o) {
-        // through LDS, so that each lane stores 4 consecutive columns of one
-        // row: lane l takes row l%16 and columns 4(l/16) ..
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
+          const f32x4 x = ao[nb] + ao2[nb];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) ot[w][(4 * lg + i) * LDO + lr] = aq[nb][i];
-          __builtin_amdgcn_wave_barrier();
-          const int r = 16 * w + lr;
-          const f32x4 x = *reinterpret_cast<const f32x4 *>(&ot[w][lr * LDO + 4 * lg]);
-          __builtin_amdgcn_wave_barrier();
-          if (r < len) {
-            const int64_t ob = ((int64_t)(t0 + r) * H_v + h) * d_v + col0 + 16 * nb + 4 * lg;
-            if constexpr (OBF16) {
-              *reinterpret_cast<u32x2 *>(static_cast<uint16_t *>(o) + ob) =
-                  u32x2{pk_bf16(x[0], x[1]), pk_bf16(x[2], x[3])};
-            } else {
-              *reinterpret_cast<f32x4 *>(static_cast<float *>(o) + ob) = x;
+          for (int i = 0; i < 4; ++i) {
+            const int r = 16 * w + 4 * lg + i;
+            if (r < len) {
+              const int64_t ob = ((int64_t)(t0 + r) * H_v + h) * d_v + col0 + 16 * nb + lr;
+              if constexpr (OBF16) static_cast<uint16_t *>(o)[ob] = f2bf(x[i]);
+              else static_cast<float *>(o)[ob] = x[i];
             }
           }
         }
       }
+      __syncthreads();  // 2
     };
 
     if (c_begin < c_end) {
-      OutOps op;
-      {
-        const u32x4 *Q4 = qp(c_begin);
-#pragma unroll
-        for (int s = 0; s < 4; ++s) op.q[s] = Q4[s * 64];
-        op.fq = fq_of(c_begin);
-        load_p(op, c_begin);
+      OutOps<NB> op0, op1;
+      load_out(op0, c_begin);
+      load_out(op1, min(c_begin + 1, c_end - 1));
+      // Past the last chunk the loads repeat it and go unused.
+      for (int c = c_begin; c < c_end; c += 2) {
+        chunk(op0, c, min(c + 2, c_end - 1));
+        if (c + 1 < c_end) chunk(op1, c + 1, min(c + 3, c_end - 1));
       }
-      chunk(op, c_begin, min(c_begin + 1, c_end - 1));
-      for (int c = c_begin + 1; c < c_end; ++c) chunk(op, c, min(c + 1, c_end - 1));
     }
   }
 }
@@ -756,9 +824,9 @@ hipError_t launch_chain(const Problem &p, const ChunkArgs &a, const Seqs &sq, hi
   const int groups = p.N * p.H_qk, ncb = p.d_v / (16 * NB);
   if (groups == 0 || ncb == 0) return hipSuccess;
   const int grid = xcd_group_grid(ncb * (p.H_v / p.H_qk), groups);
-  hipLaunchKernelGGL((wy_chain_kernel<STATES, OBF16, NB>), dim3(grid), dim3(512), 0, st, a.s0, sq, w.wf, w.pf,
-                     w.uf, w.fac, w.ktf, w.qf, a.o, a.final_state, w.u, w.sc, p.H_qk, p.H_v, p.d_v, p.max_chunks,
-                     groups);
+  hipLaunchKernelGGL((wy_chain_kernel<STATES, OBF16, NB>), dim3(grid), dim3(512), 0, st, a.s0, sq, w.wf, w.qf,
+                     w.uf, w.of, w.fac, w.ktf, a.o, a.final_state, w.u, w.sc, p.H_qk, p.H_v, p.d_v,
+                     p.max_chunks, groups);
   return hipGetLastError();
 }
 
@@ -774,8 +842,8 @@ hipError_t run_wy(const Problem &p, const ChunkArgs &a, hipStream_t st) {
   const uint16_t *q = static_cast<const uint16_t *>(a.q), *k = static_cast<const uint16_t *>(a.k),
                  *v = static_cast<const uint16_t *>(a.v);
   if (p.max_chunks > 0 && p.H_v > 0) {
-    hipLaunchKernelGGL(wy_prep_kernel, dim3(p.max_chunks, p.H_v), dim3(256), 0, st, q, k, v, a.g, a.beta,
-                       sq, w.wf, w.pf, w.uf, w.fac, w.ktf, w.qf, p.H_qk, p.H_v, p.d_v, p.max_chunks, p.scale,
+    hipLaunchKernelGGL(wy_prep_kernel, dim3(p.max_chunks * p.H_v), dim3(256), 0, st, q, k, v, a.g, a.beta,
+                       sq, w.wf, w.qf, w.uf, w.of, w.fac, w.ktf, p.H_qk, p.H_v, p.d_v, p.max_chunks, p.scale,
                        p.l2norm ? 1 : 0);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
