@@ -144,7 +144,8 @@ struct PrepSmem {
   static constexpr int R = RA > RB ? (RA > RC ? RA : RC) : (RB > RC ? RB : RC);
   alignas(16) unsigned char r[R];
   alignas(16) double gam[C];
-  float beta[C], rq[C], rk[C], eg[C];
+  alignas(16) float beta[C], rq[C], rk[C], eg[C];
+  alignas(16) float bek[C];  // beta e^G k-norm: the column scaling of T' and R'
 };
 
 __global__ __launch_bounds__(256) void wy_prep_kernel(
@@ -261,11 +262,12 @@ __global__ __launch_bounds__(256) void wy_prep_kernel(
     for (int m = 0; m < 5; ++m) {
       if (m <= w) {
         // P[r][16m + 4lg + i] = rq_r rk_i e^{G_r - G_i} (q_r . k_i), i <= r; kept in acc[m]
+        const int c0 = 16 * m + 4 * lg;
+        const f32x4 rkc = *reinterpret_cast<const f32x4 *>(sm.rk + c0);
+        const double gr = sm.gam[r];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int ci = 16 * m + 4 * lg + e;
-          acc[m][e] = ci <= r ? sm.rq[r] * sm.rk[ci] * fexp((float)(sm.gam[r] - sm.gam[ci])) * acc[m][e] : 0.f;
-        }
+        for (int e = 0; e < 4; ++e)
+          acc[m][e] = c0 + e <= r ? sm.rq[r] * rkc[e] * fexp((float)(gr - sm.gam[c0 + e])) * acc[m][e] : 0.f;
       } else {
         // A[r][i] = beta_r rk_r rk_i e^{G_r - G_i} (k_r . k_i), i < r
         const int mi = kmi[m], ni = kni[m];
@@ -281,6 +283,7 @@ __global__ __launch_bounds__(256) void wy_prep_kernel(
   }
   // Per-token factors of the carry: e^{G_last - G} (zero past the length), e^{G_last}.
   if (tid < C) {
+    sm.bek[tid] = sm.beta[tid] * sm.eg[tid] * sm.rk[tid];
     float *F = fac + slot * kWyFac;
     const double gl = sm.gam[len - 1];
     F[tid] = tid < len ? fexp((float)(gl - sm.gam[tid])) : 0.f;
@@ -413,14 +416,8 @@ __global__ __launch_bounds__(256) void wy_prep_kernel(
   // the column scalings of the four products below:
   //   diag(beta e^G k-norm): T' for W, R' for Q';   diag(beta): T'' for U', R'' for O'.
   auto frag = [&](const f32x4 &xa, const f32x4 &xb, int st, bool dk, u32x4 &hi, u32x4 &lo) {
-    f32x4 ya, yb;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int i0 = 32 * st + 4 * lg + e, i1 = i0 + 16;
-      ya[e] = xa[e] * sm.beta[i0] * (dk ? sm.eg[i0] * sm.rk[i0] : 1.f);
-      yb[e] = xb[e] * sm.beta[i1] * (dk ? sm.eg[i1] * sm.rk[i1] : 1.f);
-    }
-    split8(ya, yb, hi, lo);
+    const float *sc = (dk ? sm.bek : sm.beta) + 32 * st + 4 * lg;
+    split8(xa * *reinterpret_cast<const f32x4 *>(sc), xb * *reinterpret_cast<const f32x4 *>(sc + 16), hi, lo);
   };
   // W^T = K^T T'^T and (R' K)^T = K^T R'^T for token tile w, by d_k step s: the
   // tiles of d_k rows 32s.. and 32s+16.. give this lane row 16w + l%16 at d_k
@@ -504,11 +501,12 @@ __global__ __launch_bounds__(256) void wy_prep_kernel(
       const int ln = it & 63, ms = it >> 6, mt = ms >> 1, st = ms & 1;
       const int t = 32 * st + 4 * (ln >> 4);
       const uint32_t *r32 = reinterpret_cast<const uint32_t *>(kt + (16 * mt + (ln & 15)) * LDT + t);
-      f32x4 a, b;
-      a[0] = bf_lo(r32[0]) * sm.rk[t];      a[1] = bf_hi(r32[0]) * sm.rk[t + 1];
-      a[2] = bf_lo(r32[1]) * sm.rk[t + 2];  a[3] = bf_hi(r32[1]) * sm.rk[t + 3];
-      b[0] = bf_lo(r32[8]) * sm.rk[t + 16]; b[1] = bf_hi(r32[8]) * sm.rk[t + 17];
-      b[2] = bf_lo(r32[9]) * sm.rk[t + 18]; b[3] = bf_hi(r32[9]) * sm.rk[t + 19];
+      f32x4 a = {bf_lo(r32[0]), bf_hi(r32[0]), bf_lo(r32[1]), bf_hi(r32[1])};
+      f32x4 b = {bf_lo(r32[8]), bf_hi(r32[8]), bf_lo(r32[9]), bf_hi(r32[9])};
+      if (l2norm) {
+        a *= *reinterpret_cast<const f32x4 *>(sm.rk + t);
+        b *= *reinterpret_cast<const f32x4 *>(sm.rk + t + 16);
+      }
       K4[it] = h16x8(a, b);
     }
   }
