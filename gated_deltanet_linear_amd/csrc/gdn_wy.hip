@@ -107,6 +107,16 @@ __device__ __forceinline__ f32x2_t unpk_f16(uint32_t w) {
   return __builtin_convertvector(__builtin_bit_cast(f16x2_t, w), f32x2_t);
 }
 
+// A raw buffer resource over `bytes` bytes at p (32-bit data format): buffer
+// stores at offsets past the end are dropped by the hardware.  The chain masks
+// the rows past a ragged chunk's end this way instead of with a branch: a
+// branch around a store leaves the compiler unable to count the outstanding
+// vector-memory operations past it, and it then waits for all of them before
+// the next load is used.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(void *p, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(p, 0, (int)bytes, 0x00020000);
+}
+
 // x = hi + lo + O(2^-17 |x|) for the 4 values of a (bf16).
 __device__ __forceinline__ void split4(const f32x4 &a, u32x2 &hi, u32x2 &lo) {
   const uint32_t h0 = pk_bf16(a[0], a[1]), h1 = pk_bf16(a[2], a[3]);
@@ -659,10 +669,14 @@ __global__ __launch_bounds__(512) void wy_chain_kernel(
         reinterpret_cast<u32x2 *>(&u2x[nb][w >> 1][0][lane])[w & 1] = hi;
         reinterpret_cast<u32x2 *>(&u2x[nb][w >> 1][1][lane])[w & 1] = lo;
         if constexpr (STATES) {
+          // the write vectors of rows t0 .. t0 + len
+          const auto rs = rows_rsrc(uw + (int64_t)t0 * H_v * d_v, (int64_t)len * H_v * d_v * 4);
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const int r = 16 * w + 4 * lg + i;
-            if (r < len) uw[((int64_t)(t0 + r) * H_v + h) * d_v + col0 + 16 * nb + lr] = uv[i];
+            const float x = uv[i];  // (a bit cast of the vector element itself would read element 0)
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), rs,
+                                                  (((16 * w + 4 * lg + i) * H_v + h) * d_v + col0 + 16 * nb + lr) * 4,
+                                                  0, 0);
           }
         }
       }
@@ -738,8 +752,10 @@ __global__ __launch_bounds__(512) void wy_chain_kernel(
     // O for chunk c is formed between the chunk's two barriers, while the state
     // waves form U (the output needs S alone), and stored directly: lane l holds
     // rows 4(l/16) + i of column l%16, so each store covers 4 rows x 64 bytes,
-    // the same 64-byte row segments a transposed store would write.  Operands
-    // are loaded two chunks ahead, in two register sets used alternately.
+    // the same 64-byte row segments a transposed store would write.  The next
+    // chunk's operands are loaded right after the MFMAs that consume this
+    // chunk's, and the stores carry no branch (see rows_rsrc), so the wait for
+    // them covers those loads alone.
     auto qp = [&](int c) {
       return reinterpret_cast<const u32x4 *>(qf + (hslot + c) * kWyQBytes) + w * 4 * 64 + lane;
     };
@@ -772,18 +788,20 @@ __global__ __launch_bounds__(512) void wy_chain_kernel(
           else ao[nb] = mfma_f16(op.q[s], sv, ao[nb]);
         }
       load_out(op, cn);
-      if (o) {
+      {
+        // rows t0 .. t0 + len of o (no row without o)
+        const int esz = OBF16 ? 2 : 4;
+        const auto rs = rows_rsrc(o ? static_cast<unsigned char *>(o) + (int64_t)t0 * H_v * d_v * esz : nullptr,
+                                  o ? (int64_t)len * H_v * d_v * esz : 0);
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
           const f32x4 x = ao[nb] + ao2[nb];
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const int r = 16 * w + 4 * lg + i;
-            if (r < len) {
-              const int64_t ob = ((int64_t)(t0 + r) * H_v + h) * d_v + col0 + 16 * nb + lr;
-              if constexpr (OBF16) static_cast<uint16_t *>(o)[ob] = f2bf(x[i]);
-              else static_cast<float *>(o)[ob] = x[i];
-            }
+            const int off = (((16 * w + 4 * lg + i) * H_v + h) * d_v + col0 + 16 * nb + lr) * esz;
+            const float xi = x[i];
+            if constexpr (OBF16) __builtin_amdgcn_raw_buffer_store_b16(f2bf(xi), rs, off, 0, 0);
+            else __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(xi), rs, off, 0, 0);
           }
         }
       }
@@ -791,14 +809,12 @@ __global__ __launch_bounds__(512) void wy_chain_kernel(
     };
 
     if (c_begin < c_end) {
-      OutOps<NB> op0, op1;
-      load_out(op0, c_begin);
-      load_out(op1, min(c_begin + 1, c_end - 1));
-      // Past the last chunk the loads repeat it and go unused.
-      for (int c = c_begin; c < c_end; c += 2) {
-        chunk(op0, c, min(c + 2, c_end - 1));
-        if (c + 1 < c_end) chunk(op1, c + 1, min(c + 3, c_end - 1));
-      }
+      OutOps<NB> op;
+      load_out(op, c_begin);
+      // First chunk peeled, as on the state waves; past the last chunk the
+      // loads repeat it and go unused.
+      chunk(op, c_begin, min(c_begin + 1, c_end - 1));
+      for (int c = c_begin + 1; c < c_end; ++c) chunk(op, c, min(c + 1, c_end - 1));
     }
   }
 }
