@@ -571,6 +571,8 @@ __global__ __launch_bounds__(512) void wy_chain_kernel(
   // 16-byte load.
   __shared__ u32x4 sx[4][NB][64];
   __shared__ u32x4 u2x[NB][2][2][64];
+  constexpr int LDO = 20;  // O tile rows, fp32 (the pad spreads rows over the banks)
+  __shared__ float ot[4][16 * LDO];
   if (sq.bad()) return;
   const int NCT = d_v / 16;         // 16-column tiles of S
   const int NCB = NCT / NB;         // column blocks
@@ -750,12 +752,13 @@ __global__ __launch_bounds__(512) void wy_chain_kernel(
   } else {
     // ------------------------------ output waves -----------------------------
     // O for chunk c is formed between the chunk's two barriers, while the state
-    // waves form U (the output needs S alone), and stored directly: lane l holds
-    // rows 4(l/16) + i of column l%16, so each store covers 4 rows x 64 bytes,
-    // the same 64-byte row segments a transposed store would write.  The next
-    // chunk's operands are loaded right after the MFMAs that consume this
-    // chunk's, and the stores carry no branch (see rows_rsrc), so the wait for
-    // them covers those loads alone.
+    // waves form U (the output needs S alone).  It is stored through a small LDS
+    // transpose, so that each lane writes 4 consecutive columns of one row with
+    // one 16-byte store (a quarter of the store instructions of the accumulator
+    // layout's 4-byte ones; the vector-memory path is shared by all 8 waves).
+    // The next chunk's operands are loaded right after the MFMAs that consume
+    // this chunk's, and the stores carry no branch (see rows_rsrc), so the wait
+    // for them covers those loads alone.
     auto qp = [&](int c) {
       return reinterpret_cast<const u32x4 *>(qf + (hslot + c) * kWyQBytes) + w * 4 * 64 + lane;
     };
@@ -797,12 +800,16 @@ __global__ __launch_bounds__(512) void wy_chain_kernel(
         for (int nb = 0; nb < NB; ++nb) {
           const f32x4 x = ao[nb] + ao2[nb];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int off = (((16 * w + 4 * lg + i) * H_v + h) * d_v + col0 + 16 * nb + lr) * esz;
-            const float xi = x[i];
-            if constexpr (OBF16) __builtin_amdgcn_raw_buffer_store_b16(f2bf(xi), rs, off, 0, 0);
-            else __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(xi), rs, off, 0, 0);
-          }
+          for (int i = 0; i < 4; ++i) ot[w][(4 * lg + i) * LDO + lr] = x[i];
+          __builtin_amdgcn_wave_barrier();
+          const f32x4 y = *reinterpret_cast<const f32x4 *>(&ot[w][lr * LDO + 4 * lg]);
+          __builtin_amdgcn_wave_barrier();
+          // lane l: row 16w + l%16, columns col0 + 16nb + 4(l/16) ..
+          const int off = (((16 * w + lr) * H_v + h) * d_v + col0 + 16 * nb + 4 * lg) * esz;
+          if constexpr (OBF16)
+            __builtin_amdgcn_raw_buffer_store_b64(u32x2{pk_bf16(y[0], y[1]), pk_bf16(y[2], y[3])}, rs, off, 0, 0);
+          else
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, y), rs, off, 0, 0);
         }
       }
       __syncthreads();  // 2
