@@ -153,7 +153,7 @@ def chunk_work(tokens, H_v, d_k=128, d_v=128, C=64):
     6 d_k d_v (state terms) + C (3 d_k + 2 d_v) (intra-chunk products) + C^2/3 (solve) FLOP;
     bytes: q, k at query/key-head width (128 + 128), v 256, o fp32 512, g and beta 4 + 4."""
     flop = 6 * d_k * d_v + C * (3 * d_k + 2 * d_v) + C * C / 3
-    carry_flop = 6 * d_k * d_v + 2 * C * d_v   # the carry kernel's share: state terms, T X, P U
+    carry_flop = 6 * d_k * d_v   # the chain kernel's share: the three products with the state
     nbytes = 128 + 128 + 256 + 512 + 4 + 4
     carry_bytes = 128 + 128 + 256 + 512
     th = tokens * H_v
@@ -221,7 +221,8 @@ def main():
     log(f"prefill: {ms * 1e3:.1f} us/step, kernels(us) " +
         ", ".join(f"{k}={v * 1e3:.1f}" for k, v in kern.items()))
     # the chain kernel (state carry) dominates; its algorithmic work is its share of
-    # the method's FLOPs (state terms and P U), priced against dense bf16 MFMA
+    # the method's FLOPs (the three state products W S, K^T U, Q' S), priced
+    # against dense bf16 MFMA
     rl = roofline("mfma", cflop / (kd / 1e3) / 1e12, MFMA_BF16_PEAK_TFLOPS, "TFLOP/s",
                   traffic=measured_traffic("wy_chain_kernel"), kernel="wy_chain_kernel",
                   kernel_us=round(kd * 1e3, 2), algorithmic_flop=cflop,
