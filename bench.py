@@ -77,8 +77,9 @@ class Prepared:
             raise RuntimeError(self.lib.gdn_last_error().decode())
 
 
-def prepare_chunk(lib, b, d, states=False):
-    """Bind a gdn_chunk_fwd (or gdn_states_fwd) call on device inputs d."""
+def prepare_chunk(lib, b, d, states=False, select=None):
+    """Bind a gdn_chunk_fwd (or gdn_states_fwd) call on device inputs d; with states and
+    select = (t_begin, t_end, t_step), a gdn_states_fwd_strided call."""
     import torch
     P = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())
     B, T, H_qk, d_k = d["q"].shape
@@ -93,11 +94,18 @@ def prepare_chunk(lib, b, d, states=False):
     if states:
         need = lib.gdn_states_fwd_workspace(ctypes.byref(s), nseq)
         ws = torch.empty(need, dtype=torch.uint8, device=dev)
-        st = torch.empty((B, T, H_v, d_k, d_v), dtype=torch.float32, device=dev)
-        args = [P(d["q"]), P(d["k"]), P(d["v"]), P(d["g"]), P(d["beta"]), P(d["s0"]), P(d["cu"]), nseq,
-                P(o), P(st), P(fin), P(ws), need, stream]
+        if select is None:
+            st = torch.empty((B, T, H_v, d_k, d_v), dtype=torch.float32, device=dev)
+            args = [P(d["q"]), P(d["k"]), P(d["v"]), P(d["g"]), P(d["beta"]), P(d["s0"]), P(d["cu"]), nseq,
+                    P(o), P(st), P(fin), P(ws), need, stream]
+            fn = lib.gdn_states_fwd
+        else:
+            t0, t1, step = select
+            st = torch.empty((B, len(range(t0, t1, step)), H_v, d_k, d_v), dtype=torch.float32, device=dev)
+            args = [P(d["q"]), P(d["k"]), P(d["v"]), P(d["g"]), P(d["beta"]), P(d["s0"]), P(d["cu"]), nseq,
+                    P(o), P(st), t0, t1, step, P(fin), P(ws), need, stream]
+            fn = lib.gdn_states_fwd_strided
         keep = (o, fin, ws, st)
-        fn = lib.gdn_states_fwd
     else:
         need = lib.gdn_chunk_fwd_workspace(ctypes.byref(s), nseq)
         ws = torch.empty(need, dtype=torch.uint8, device=dev)
@@ -326,7 +334,16 @@ def main():
                                  algorithmic_bytes=sbytes),
             "path_hbm_frac": round((sbytes + ws_.T * ws_.H_v * 1032) / (mss / 1e3) / 1e9 / HBM_PEAK_GBS, 4)}
         log(f"states: {mss * 1e3:.1f} us/call")
-        del dsx, calls
+        del calls
+        # the same call keeping one state per 64-token chunk (the chunk-boundary states)
+        callx = prepare_chunk(lib, b, dsx, states=True, select=(63, ws_.T, 64))
+        msx, kx_ = timed_chunk_calls(lib, [callx], 10, 3, 4)
+        result["states"]["strided_t_step_64"] = {
+            "us_per_call": round(msx * 1e3, 2), "tokens_per_s": round(ws_.T / (msx / 1e3), 1),
+            "states_kept": len(range(63, ws_.T, 64)),
+            "kernel_us": {k: round(v * 1e3, 2) for k, v in zip(["plan", "prep", "carry", "stream"], kx_)}}
+        log(f"states, one per chunk: {msx * 1e3:.1f} us/call")
+        del dsx, callx
 
     # ---- the fp64 CPU oracle on the host, on the same workload -------------------------
     if not args.no_cpu:

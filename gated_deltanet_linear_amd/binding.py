@@ -37,7 +37,7 @@ class GdnShape(ctypes.Structure):
 
 
 EXPORTS = ("gdn_chunk_fwd", "gdn_chunk_fwd_workspace", "gdn_recurrent_step", "gdn_states_fwd",
-           "gdn_states_fwd_workspace", "gdn_gated_norm", "gdn_recurrent_step_gated",
+           "gdn_states_fwd_strided", "gdn_states_fwd_workspace", "gdn_gated_norm", "gdn_recurrent_step_gated",
            "gdn_mixer_prologue", "gdn_set_timing_events", "gdn_status_string",
            "gdn_last_error", "gdn_version")
 
@@ -61,6 +61,8 @@ def load_library(path: Optional[str] = None):
     lib.gdn_chunk_fwd_workspace.argtypes = [S, I]
     lib.gdn_states_fwd.restype = ctypes.c_int
     lib.gdn_states_fwd.argtypes = [S, P, P, P, P, P, P, P, I, P, P, P, P, Z, P]
+    lib.gdn_states_fwd_strided.restype = ctypes.c_int
+    lib.gdn_states_fwd_strided.argtypes = [S, P, P, P, P, P, P, P, I, P, P, I, I, I, P, P, Z, P]
     lib.gdn_states_fwd_workspace.restype = Z
     lib.gdn_states_fwd_workspace.argtypes = [S, I]
     lib.gdn_recurrent_step.restype = ctypes.c_int
@@ -191,18 +193,28 @@ def gdn_chunk_fwd(q, k, v, g, beta, initial_state=None, cu_seqlens=None, scale=N
 
 def gdn_states_fwd(q, k, v, g, beta, initial_state=None, cu_seqlens=None, scale=None, chunk=None,
                    l2norm=False, o_dtype=torch.float32, want_o=True, output_final_state=True,
-                   states=None, o=None, final_state=None, workspace=None):
-    """gdn_chunk_fwd plus every per-token state.  Returns (o or None, states, final or None)."""
+                   states=None, o=None, final_state=None, workspace=None, t_begin=0, t_end=None, t_step=1):
+    """gdn_chunk_fwd plus the per-token states.  Returns (o or None, states, final or None).
+
+    With the default selection every token's state is kept (states [B, T, H_v, d_k, d_v]); otherwise
+    the tokens t_begin, t_begin + t_step, ... < t_end of every row (gdn_states_fwd_strided; states
+    [B, n, H_v, d_k, d_v], n = ceil((t_end - t_begin) / t_step))."""
     lib = load_library()
     dev, B, T, H_qk, H_v, d_k, d_v, N = _common(q, k, v, g, beta, initial_state, cu_seqlens)
     s = _shape(q, v, chunk, scale, l2norm, o_dtype, B, T)
+    t_end = T if t_end is None else int(t_end)
+    t_begin, t_step = int(t_begin), int(t_step)
+    strided = (t_begin, t_end, t_step) != (0, T, 1)
+    if not (0 <= t_begin <= t_end <= T and t_step >= 1):
+        raise GdnError(2, f"token selection [{t_begin}, {t_end}) step {t_step} is not within [0, {T})")
+    n_sel = (t_end - t_begin + t_step - 1) // t_step
     if want_o and o is None:
         o = torch.empty((B, T, H_v, d_v), dtype=o_dtype, device=dev)
     if o is not None:
         _need(o, "o", (B, T, H_v, d_v), o_dtype, dev)
     if states is None:
-        states = torch.empty((B, T, H_v, d_k, d_v), dtype=torch.float32, device=dev)
-    _need(states, "states", (B, T, H_v, d_k, d_v), torch.float32, dev)
+        states = torch.empty((B, n_sel, H_v, d_k, d_v), dtype=torch.float32, device=dev)
+    _need(states, "states", (B, n_sel, H_v, d_k, d_v), torch.float32, dev)
     if output_final_state and final_state is None:
         final_state = torch.empty((N, H_v, d_k, d_v), dtype=torch.float32, device=dev)
     if final_state is not None:
@@ -214,6 +226,13 @@ def gdn_states_fwd(q, k, v, g, beta, initial_state=None, cu_seqlens=None, scale=
                                        None), "gdn_states_fwd")
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    if strided:
+        st = lib.gdn_states_fwd_strided(ctypes.byref(s), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                        _ptr(initial_state), _ptr(cu_seqlens), nseq, _ptr(o), _ptr(states),
+                                        t_begin, t_end, t_step, _ptr(final_state), _ptr(workspace),
+                                        workspace.numel() * workspace.element_size(), _stream(dev))
+        _check(lib, st, "gdn_states_fwd_strided")
+        return o, states, final_state
     st = lib.gdn_states_fwd(ctypes.byref(s), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                             _ptr(initial_state), _ptr(cu_seqlens), nseq, _ptr(o), _ptr(states),
                             _ptr(final_state), _ptr(workspace),

@@ -107,7 +107,7 @@ struct Tensors {
 
 Tensors spans(const gdn::Problem &p, const void *q, const void *k, const void *v, const float *g,
               const float *beta, const float *s0, const int32_t *cu, const void *o, const float *states,
-              const float *fin, const void *ws, size_t ws_bytes) {
+              size_t states_tokens, const float *fin, const void *ws, size_t ws_bytes) {
   const size_t T = p.T_tot, es = esize(p.dtype);
   const size_t state_bytes = (size_t)p.N * p.H_v * p.d_k * p.d_v * sizeof(float);
   Tensors t;
@@ -119,7 +119,7 @@ Tensors spans(const gdn::Problem &p, const void *q, const void *k, const void *v
   t.s0 = Span(s0, state_bytes);
   t.cu = Span(cu, ((size_t)p.N + 1) * sizeof(int32_t));
   t.o = Span(o, T * p.H_v * p.d_v * esize(p.o_dtype));
-  t.states = Span(states, T * p.H_v * p.d_k * p.d_v * sizeof(float));
+  t.states = Span(states, states_tokens * p.H_v * p.d_k * p.d_v * sizeof(float));
   t.fin = Span(fin, state_bytes);
   t.ws = Span(ws, ws_bytes);
   return t;
@@ -128,17 +128,24 @@ Tensors spans(const gdn::Problem &p, const void *q, const void *k, const void *v
 gdn_status chunked_common(const gdn_shape *s, const void *q, const void *k, const void *v, const float *g,
                           const float *beta, const float *initial_state, const int32_t *cu_seqlens,
                           int32_t num_seqs, void *o, float *states, float *final_state, void *workspace,
-                          size_t workspace_bytes, hipStream_t stream, bool with_states) {
+                          size_t workspace_bytes, hipStream_t stream, bool with_states, int32_t t_begin = 0,
+                          int32_t t_end = -1, int32_t t_step = 1) {
   gdn::Problem p;
   gdn_status st = check_shape(s, cu_seqlens != nullptr, num_seqs, 0, p);
   if (st != GDN_OK) return st;
+  // the token selection of the states path (all tokens unless strided)
+  if (t_end < 0) t_end = p.T;
+  if (with_states && (t_begin < 0 || t_end > p.T || t_begin > t_end || t_step < 1))
+    return fail(GDN_ERR_SHAPE, "token selection [%d, %d) step %d is not within [0, %d) with step >= 1", t_begin,
+                t_end, t_step, p.T);
+  const int32_t n_sel = with_states ? (t_end - t_begin + t_step - 1) / t_step : 0;
   if (!gdn::chunk_path_supported(p))
     return fail(GDN_ERR_UNSUPPORTED, "no chunked kernel for dtype=%d d_k=%d d_v=%d chunk=%d", p.dtype, p.d_k,
                 p.d_v, p.C);
   const bool any_tokens = p.T_tot > 0;
   if (any_tokens && (!q || !k || !v || !g || !beta)) return fail(GDN_ERR_NULL, "q, k, v, g and beta are required");
   if (!with_states && any_tokens && !o) return fail(GDN_ERR_NULL, "o is required");
-  if (with_states && any_tokens && !states) return fail(GDN_ERR_NULL, "states is required");
+  if (with_states && n_sel > 0 && p.B > 0 && !states) return fail(GDN_ERR_NULL, "states is required");
   const gdn::Workspace need = gdn::workspace_layout(p, with_states, nullptr);
   if (!workspace) return fail(GDN_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need.bytes);
   if (workspace_bytes < need.bytes)
@@ -154,8 +161,8 @@ gdn_status chunked_common(const gdn_shape *s, const void *q, const void *k, cons
                       {workspace, "workspace", 16}};
   if ((st = check_alignment(args)) != GDN_OK) return st;
 
-  const Tensors t = spans(p, q, k, v, g, beta, initial_state, cu_seqlens, o, states, final_state, workspace,
-                          workspace_bytes);
+  const Tensors t = spans(p, q, k, v, g, beta, initial_state, cu_seqlens, o, states,
+                          with_states ? (size_t)p.B * n_sel : 0, final_state, workspace, workspace_bytes);
   const Span ins[] = {t.q, t.k, t.v, t.g, t.beta, t.s0, t.cu};
   const char *in_names[] = {"q", "k", "v", "g", "beta", "initial_state", "cu_seqlens"};
   struct Out {
@@ -185,6 +192,10 @@ gdn_status chunked_common(const gdn_shape *s, const void *q, const void *k, cons
   a.o = o;
   a.final_state = final_state;
   a.states = states;
+  a.t_lo = t_begin;
+  a.t_hi = t_end;
+  a.t_step = t_step;
+  a.n_sel = n_sel;
   a.ws = gdn::workspace_layout(p, with_states, workspace);
   a.events = g_events;
   a.n_events = g_n_events;
@@ -269,6 +280,21 @@ gdn_status gdn_states_fwd(const gdn_shape *s, const void *q, const void *k, cons
   }
 }
 
+gdn_status gdn_states_fwd_strided(const gdn_shape *s, const void *q, const void *k, const void *v,
+                                  const float *g, const float *beta, const float *initial_state,
+                                  const int32_t *cu_seqlens, int32_t num_seqs, void *o, float *states,
+                                  int32_t t_begin, int32_t t_end, int32_t t_step, float *final_state,
+                                  void *workspace, size_t workspace_bytes, hipStream_t stream) {
+  try {
+    return chunked_common(s, q, k, v, g, beta, initial_state, cu_seqlens, num_seqs, o, states, final_state,
+                          workspace, workspace_bytes, stream, true, t_begin, t_end, t_step);
+  } catch (const std::exception &e) {
+    return fail(GDN_ERR_HIP, "internal error: %s", e.what());
+  } catch (...) {
+    return fail(GDN_ERR_HIP, "internal error");
+  }
+}
+
 gdn_status gdn_recurrent_step(const gdn_shape *s, const void *q, const void *k, const void *v, const float *g,
                               const float *beta, float *state, void *o, hipStream_t stream) {
   try {
@@ -284,7 +310,7 @@ gdn_status gdn_recurrent_step(const gdn_shape *s, const void *q, const void *k, 
                         {g, "g", 4},              {beta, "beta", 4},          {state, "state", 16},
                         {o, "o", 4 * esize(p.o_dtype)}};
     if ((st = check_alignment(args)) != GDN_OK) return st;
-    const Tensors t = spans(p, q, k, v, g, beta, nullptr, nullptr, o, nullptr, nullptr, nullptr, 0);
+    const Tensors t = spans(p, q, k, v, g, beta, nullptr, nullptr, o, nullptr, 0, nullptr, nullptr, 0);
     const Span sst(state, (size_t)p.B * p.H_v * p.d_k * p.d_v * sizeof(float));
     const Span ins[] = {t.q, t.k, t.v, t.g, t.beta};
     const char *in_names[] = {"q", "k", "v", "g", "beta"};
@@ -319,7 +345,7 @@ gdn_status gdn_recurrent_step_gated(const gdn_shape *s, const void *q, const voi
                         {g, "g", 4},              {beta, "beta", 4},            {state, "state", 16},
                         {z, "z", esize(p.dtype)}, {weight, "weight", 4},        {out, "out", 4 * esize(p.o_dtype)}};
     if ((st = check_alignment(args)) != GDN_OK) return st;
-    const Tensors t = spans(p, q, k, v, g, beta, nullptr, nullptr, out, nullptr, nullptr, nullptr, 0);
+    const Tensors t = spans(p, q, k, v, g, beta, nullptr, nullptr, out, nullptr, 0, nullptr, nullptr, 0);
     const Span sst(state, (size_t)p.B * p.H_v * p.d_k * p.d_v * sizeof(float));
     const Span sz(z, (size_t)p.B * p.H_v * p.d_v * esize(p.dtype)), sw(weight, (size_t)p.d_v * sizeof(float));
     const Span ins[] = {t.q, t.k, t.v, t.g, t.beta, sz, sw};

@@ -737,12 +737,15 @@ __global__ __launch_bounds__(512) void carry_kernel(
 // (chunk, value head, block of RS * SRPT rows of S); a thread owns 4 columns of
 // SRPT rows (rows rl + RS i), so that each wave store covers consecutive rows,
 // and streams them out token by token with non-temporal 16-byte stores.
+// Only the selected tokens are stored: tl = t_lo + j t_step < t_hi, tl the
+// token's index in its row of rowT tokens, to states[row * n_sel + j]; a chunk
+// with no selected token is skipped.
 // ---------------------------------------------------------------------------
 template <typename TIn, int C, int SRPT>
 __global__ __launch_bounds__(256) void stream_kernel(
     const TIn *__restrict__ k, const float *__restrict__ g, const float *__restrict__ uw,
     const float *__restrict__ scw, const Seqs sq, float *__restrict__ states, int H_qk, int H_v, int d_k,
-    int d_v, int l2norm) {
+    int d_v, int l2norm, int rowT, int t_lo, int t_hi, int t_step, int n_sel) {
   extern __shared__ float ssm[];  // u [C][d_v], kk [C][RS][SRPT], alpha [C]
   static_assert(SRPT % 4 == 0 || SRPT == 1, "k factors are read 4 at a time");
   if (sq.bad()) return;
@@ -752,6 +755,15 @@ __global__ __launch_bounds__(256) void stream_kernel(
   const int t0 = sq.start(n) + (c - sq.first(n)) * C;
   const int len = min(C, sq.start(n + 1) - t0);
   const int h = blockIdx.y, j = h / (H_v / H_qk);
+  // the chunk's tokens lie in one row: row b, in-row indices tl0 .. tl0 + len
+  const int brow = t0 / rowT, tl0 = t0 - brow * rowT;
+  int r_end;  // tokens of the chunk to step through: up to its last selected one
+  {
+    const int f = max(t_lo, tl0), e = min(t_hi, tl0 + len);
+    const int first = t_lo + (f - t_lo + t_step - 1) / t_step * t_step;  // first selected in-row index >= f
+    if (first >= e) return;
+    r_end = t_lo + (e - 1 - t_lo) / t_step * t_step - tl0 + 1;
+  }
   const int CGn = d_v / 4, RS = 256 / CGn, SR = RS * SRPT;
   const int row0 = blockIdx.z * SR;
   const int tid = threadIdx.x, cg = tid % CGn, rl = tid / CGn;
@@ -786,14 +798,14 @@ __global__ __launch_bounds__(256) void stream_kernel(
   f32x4 Sv[SRPT];
   const int64_t sstride = (int64_t)H_v * d_k * d_v;  // one token
   const int64_t rstride = (int64_t)RS * d_v;          // from row i to row i + 1 of this thread
-  float *dst = states + ((int64_t)t0 * H_v + h) * d_k * d_v + (int64_t)(row0 + rl) * d_v + 4 * cg;
+  float *dst0 = states + (int64_t)h * d_k * d_v + (int64_t)(row0 + rl) * d_v + 4 * cg;
 #pragma unroll
   for (int i = 0; i < SRPT; ++i) {
     const int row = min(row0 + rl + RS * i, d_k - 1);  // rows past d_k: computed, not stored
     Sv[i] = *reinterpret_cast<const f32x4 *>(scw + (slot * d_k + row) * d_v + 4 * cg);
   }
   const bool full = row0 + SR <= d_k;
-  for (int r = 0; r < len; ++r) {
+  for (int r = 0; r < r_end; ++r) {
     const f32x4 uv = *reinterpret_cast<const f32x4 *>(us + r * d_v + 4 * cg);
     const float a = al[r];
     float kf[SRPT];
@@ -808,12 +820,15 @@ __global__ __launch_bounds__(256) void stream_kernel(
       }
     }
 #pragma unroll
-    for (int i = 0; i < SRPT; ++i) {
-      Sv[i] = a * Sv[i] + kf[i] * uv;
-      if (full || row0 + rl + RS * i < d_k)
-        __builtin_nontemporal_store(Sv[i], reinterpret_cast<f32x4 *>(dst + i * rstride));
+    for (int i = 0; i < SRPT; ++i) Sv[i] = a * Sv[i] + kf[i] * uv;
+    const int tl = tl0 + r;
+    if (tl >= t_lo && tl < t_hi && (tl - t_lo) % t_step == 0) {  // uniform over the block
+      float *dst = dst0 + ((int64_t)brow * n_sel + (tl - t_lo) / t_step) * sstride;
+#pragma unroll
+      for (int i = 0; i < SRPT; ++i)
+        if (full || row0 + rl + RS * i < d_k)
+          __builtin_nontemporal_store(Sv[i], reinterpret_cast<f32x4 *>(dst + i * rstride));
     }
-    dst += sstride;
   }
 }
 
@@ -834,9 +849,11 @@ static hipError_t stream_t(const Problem &p, const ChunkArgs &a, const Seqs &sq,
   const int zb = ceil_div(p.d_k, SR);
   if (p.max_chunks > 0 && p.H_v > 0 && zb > 0) {
     const size_t shm = sizeof(float) * ((size_t)C * p.d_v + (size_t)C * SR + C);
+    if (a.n_sel <= 0) return hipSuccess;
+    const int rowT = p.packed ? p.T_tot : p.T;
     hipLaunchKernelGGL((stream_kernel<TIn, C, SRPT>), dim3(p.max_chunks, p.H_v, zb), dim3(256), shm, st,
                        static_cast<const TIn *>(a.k), a.g, w.u, w.sc, sq, a.states, p.H_qk, p.H_v, p.d_k, p.d_v,
-                       p.l2norm ? 1 : 0);
+                       p.l2norm ? 1 : 0, rowT, a.t_lo, a.t_hi, a.t_step, a.n_sel);
     return hipGetLastError();
   }
   return hipSuccess;

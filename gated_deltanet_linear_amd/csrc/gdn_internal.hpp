@@ -69,6 +69,10 @@ struct ChunkArgs {
   void *o;             // may be null (states path)
   float *final_state;  // may be null
   float *states;       // states path only
+  // states path: keep the tokens t_lo, t_lo + t_step, ... < t_hi of every row
+  // (the T axis of [B, T]; with cu_seqlens, of the one packed row); states then
+  // holds n_sel = ceil((t_hi - t_lo) / t_step) tokens per row
+  int t_lo = 0, t_hi = 0, t_step = 1, n_sel = 0;
   Workspace ws;
   hipEvent_t *events = nullptr;  // optional timing hook: recorded around each launch
   int n_events = 0;

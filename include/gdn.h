@@ -158,6 +158,36 @@ gdn_status gdn_states_fwd(const gdn_shape *s, const void *q, const void *k,
 size_t gdn_states_fwd_workspace(const gdn_shape *s, int32_t num_seqs);
 
 /*
+ * gdn_states_fwd_strided: gdn_states_fwd keeping only some tokens' states.
+ * The Qwen3.5 text encyclopedia page gives both the per-token `states` [batch
+ * seq heads key_dim value_dim], at 1-3 MiB per token per block (note
+ * "Loading"), and `state`, the state after one token, read by iterating over
+ * the prompt's tokens (value table of model.layers[i].linear_attn); this call
+ * writes the states of a token range at a stride, and only those.
+ *
+ *   t_begin, t_end, t_step  the tokens kept are t_begin, t_begin + t_step, ...
+ *                           < t_end of every row, indexed along the T axis of
+ *                           the [B, T] token layout (with cu_seqlens: along the
+ *                           one packed row).  0 <= t_begin <= t_end <= T and
+ *                           t_step >= 1, else GDN_ERR_SHAPE.
+ *   states  [B, n, H_v, d_k, d_v] float32 (written), n = ceil((t_end - t_begin)
+ *           / t_step): states[b, i, h] is S after token t_begin + i t_step of
+ *           row b.  May be NULL only when n == 0; must not overlap any other
+ *           argument.
+ * o and final_state are complete, as in gdn_states_fwd; the workspace is the one
+ * gdn_states_fwd_workspace returns.  t_begin = 0, t_end = T, t_step = 1 gives
+ * gdn_states_fwd.  Only the kept states are written to memory: the state write,
+ * the bulk of the call's traffic, shrinks in proportion.
+ */
+gdn_status gdn_states_fwd_strided(const gdn_shape *s, const void *q, const void *k,
+                                  const void *v, const float *g, const float *beta,
+                                  const float *initial_state, const int32_t *cu_seqlens,
+                                  int32_t num_seqs, void *o, float *states, int32_t t_begin,
+                                  int32_t t_end, int32_t t_step, float *final_state,
+                                  void *workspace, size_t workspace_bytes,
+                                  hipStream_t stream);
+
+/*
  * The mixer's steps around the delta rule (Qwen3.5 text encyclopedia page,
  * note "The DeltaNet mixer"; Qwen3-Next encyclopedia page, same note):
  *

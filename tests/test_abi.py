@@ -85,3 +85,25 @@ def test_workspace_query_matches_layout():
     per = 2 * 64 * 64 * 4 + 2 * 64 * 4                                  # T diag(beta), P, eg, eb
     assert w >= chunks * 32 * per
     assert ws >= w + 4096 * 32 * 128 * 4 + chunks * 32 * 128 * 128 * 4
+
+
+def test_strided_states_selection_is_validated():
+    """gdn_states_fwd_strided refuses a token selection outside [0, T) or a step below 1, and
+    sizes states by the selection (an overlap with the selection's extent is refused)."""
+    lib = _lib()
+    s = _shape()   # T = 128
+    need = lib.gdn_states_fwd_workspace(ctypes.byref(s), 0)
+    q, k, v, g, b, o, st, fin, ws = _ptrs(9)
+
+    def call(t0, t1, step, states=st):
+        return lib.gdn_states_fwd_strided(ctypes.byref(s), q, k, v, g, b, None, None, 0, o, states,
+                                          t0, t1, step, fin, ws, need, None)
+    assert call(-1, 128, 1) == 2
+    assert call(0, 129, 1) == 2
+    assert call(5, 4, 1) == 2
+    assert call(0, 128, 0) == 2
+    assert b"token selection" in lib.gdn_last_error()
+    assert call(0, 128, 1, states=None) == 1
+    # 3 selected tokens of 32 heads x 128 x 128 fp32 = 6 MiB of states: placed to end inside v
+    states = ctypes.c_void_p(v.value - 2 * 1024 * 1024)
+    assert call(0, 128, 50, states=states) == 5

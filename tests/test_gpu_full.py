@@ -120,3 +120,24 @@ def test_states_t2048():
         e_rel = rel_max(host(ot), host(o[0, t]))
         print(f"o_t vs S_t^T q_t at t={t}: {e_rel:.3e}", flush=True)
         assert e_rel <= 5e-3
+
+
+def test_states_t2048_strided():
+    """The states workload read at one state per 64-token chunk and over a token range: the
+    selected states against the oracle (sampled heads) and bit-identical to the full readout's."""
+    gdn = _gdn()
+    inp = synth.make_inputs(synth.WORKLOADS["states_t2048"], seed=0)
+    d = to_dev(inp)
+    heads = [0, 31]
+    ref = gdn_ref.recurrent(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], heads=heads,
+                            want_states=True)
+    for t0, t1, step in ((63, 2048, 64), (1000, 1100, 1)):
+        o, st, fin = gdn.gdn_states_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], t_begin=t0, t_end=t1,
+                                        t_step=step)
+        torch.cuda.synchronize()
+        es = rel_fro(host(st[:, :, heads]), ref["states"][:, t0:t1:step])
+        print(f"strided states [{t0}, {t1}) step {step}: rel = {es:.3e}", flush=True)
+        assert es <= TOL_BF16_STATE
+        if step == 64:
+            assert rel_fro(host(st[:, -1]), host(fin)) <= 1e-5     # token 2047 is the last
+        del o, st, fin

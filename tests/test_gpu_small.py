@@ -217,6 +217,56 @@ def test_states_match_oracle_and_final():
     assert rel_fro(host(st[:, -1]), host(fin)) <= 1e-5
 
 
+def test_strided_states_fp32_and_bf16():
+    """gdn_states_fwd_strided keeps the tokens t_begin, t_begin + t_step, ... < t_end of every row:
+    the oracle's per-token states at those tokens (selection is plain indexing of the recurrence's
+    states), with o and the final state complete.  fp32 path (d = 16, chunk 16) to 1e-4 RMS; bf16
+    path over four rows and a ragged tail, the selection starting mid-chunk and crossing chunks."""
+    gdn = _lib()
+    inp = synth.make_inputs(synth.WORKLOADS["tiny_fp32"], seed=0)
+    d = to_dev(inp)
+    ref = _ref(inp, want_states=True)
+    for t0, t1, step in ((3, 50, 7), (0, 64, 16), (63, 64, 1), (10, 10, 3)):
+        o, st, fin = gdn.gdn_states_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], chunk=16,
+                                        t_begin=t0, t_end=t1, t_step=step)
+        torch.cuda.synchronize()
+        assert st.shape[1] == len(range(t0, t1, step))
+        if st.shape[1]:
+            assert rel_max(host(st), ref["states"][:, t0:t1:step]) <= TOL_F32
+        assert rel_max(host(o), ref["o"]) <= TOL_F32
+        assert rel_max(host(fin), ref["final"]) <= TOL_F32
+
+    inp = _bf16_case(T=150, seed=21, s0_std=0.02, B=4)
+    d = to_dev(inp)
+    heads = [0, 13, 31]
+    ref = _ref(inp, heads=heads, want_states=True)
+    o, st_all, fin = gdn.gdn_states_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], initial_state=d["s0"])
+    for t0, t1, step in ((5, 150, 64), (37, 101, 1), (149, 150, 5)):
+        o2, st, fin2 = gdn.gdn_states_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], initial_state=d["s0"],
+                                          t_begin=t0, t_end=t1, t_step=step)
+        torch.cuda.synchronize()
+        assert rel_fro(host(st[:, :, heads]), ref["states"][:, t0:t1:step]) <= TOL_BF16_STATE
+        # the same kernels as the full readout: the kept states are its states, bit for bit
+        assert torch.equal(st, st_all[:, t0:t1:step])
+        assert torch.equal(o2, o) and torch.equal(fin2, fin)
+
+
+def test_strided_states_packed_rows():
+    """With cu_seqlens the selection runs along the one packed row, across sequence boundaries."""
+    gdn = _lib()
+    lengths = (70, 0, 131, 5)
+    inp = synth.make_inputs(synth.WORKLOADS["packed_8seq"], seed=22, lengths=lengths)
+    d = to_dev(inp)
+    heads = [2, 30]
+    ref = _ref(inp, heads=heads, want_states=True)
+    t0, t1, step = 3, sum(lengths), 9
+    o, st, fin = gdn.gdn_states_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], initial_state=d["s0"],
+                                    cu_seqlens=d["cu"], t_begin=t0, t_end=t1, t_step=step)
+    torch.cuda.synchronize()
+    assert st.shape[:2] == (1, len(range(t0, t1, step)))
+    assert rel_fro(host(st[:, :, heads]), ref["states"][:, t0:t1:step]) <= TOL_BF16_STATE
+
+
 def test_many_rows_both_paths():
     """Four rows of 32 heads: enough (row, head) pairs that the carry runs on 32-column
     blocks of the state (the layout for launches that fill every compute unit)."""
