@@ -543,8 +543,9 @@ __global__ __launch_bounds__(256) void wy_prep_kernel(
 // use, interleaved with the MFMAs of its phase).
 //
 // NB = 1 gives the most blocks (the latency of one long sequence is spread over
-// every CU); NB = 2 halves the operand loads per column of S, for launches that
-// fill the GPU with blocks either way (many sequences, or many heads).
+// every CU); NB = 2 and 4 cut the operand loads per column of S by 2 and 4, for
+// launches that fill the GPU with blocks either way (many sequences, or many
+// heads).
 // ---------------------------------------------------------------------------
 template <int NB> struct StateOps {
   u32x4 w[4];      // W (fp16) of token tile w, d_k steps 0..3
@@ -869,11 +870,16 @@ hipError_t run_wy(const Problem &p, const ChunkArgs &a, hipStream_t st) {
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   mark_event(a, 2, st);
-  // 32-column blocks once 16-column blocks would fill every CU twice over.
-  const bool wide = p.N * p.H_v * (p.d_v / 16) >= 2 * device_cus();
-  if ((e = wide ? launch_chain<STATES, OBF16, 2>(p, a, sq, st) : launch_chain<STATES, OBF16, 1>(p, a, sq, st)) !=
-      hipSuccess)
-    return e;
+  // Column blocks of 16, 32 or 64 columns: the width doubles while the narrower
+  // blocks would fill every CU twice over (wider blocks load each chunk's W,
+  // K^T and Q' once for more columns; narrower ones spread a few long chains
+  // over more CUs).
+  const int64_t chains16 = (int64_t)p.N * p.H_v * (p.d_v / 16), fill = 2 * (int64_t)device_cus();
+  const int nb = chains16 >= fill ? (p.d_v % 64 == 0 && chains16 / 2 >= fill ? 4 : 2) : 1;
+  e = nb == 4 ? launch_chain<STATES, OBF16, 4>(p, a, sq, st)
+      : nb == 2 ? launch_chain<STATES, OBF16, 2>(p, a, sq, st)
+                : launch_chain<STATES, OBF16, 1>(p, a, sq, st);
+  if (e != hipSuccess) return e;
   mark_event(a, 3, st);
   if constexpr (STATES) {
     if ((e = launch_states_stream(p, a, sq, st)) != hipSuccess) return e;

@@ -267,11 +267,13 @@ def test_strided_states_packed_rows():
     assert rel_fro(host(st[:, :, heads]), ref["states"][:, t0:t1:step]) <= TOL_BF16_STATE
 
 
-def test_many_rows_both_paths():
-    """Four rows of 32 heads: enough (row, head) pairs that the carry runs on 32-column
-    blocks of the state (the layout for launches that fill every compute unit)."""
+@pytest.mark.parametrize("B", [2, 4])
+def test_many_rows_both_paths(B):
+    """Two or four rows of 32 heads: enough (row, head) pairs that the carry runs on 32-column
+    (B = 2) or 64-column (B = 4) blocks of the state, the layouts for launches that fill every
+    compute unit."""
     gdn = _lib()
-    inp = _bf16_case(T=150, seed=16, s0_std=0.02, B=4)
+    inp = _bf16_case(T=150, seed=16, s0_std=0.02, B=B)
     d = to_dev(inp)
     heads = [0, 13, 31]
     ref = _ref(inp, heads=heads, want_states=True)
