@@ -267,6 +267,28 @@ def test_strided_states_packed_rows():
     assert rel_fro(host(st[:, :, heads]), ref["states"][:, t0:t1:step]) <= TOL_BF16_STATE
 
 
+@pytest.mark.parametrize("d_v", [32, 64, 96])
+@pytest.mark.parametrize("B", [1, 8])
+def test_other_value_widths(d_v, B):
+    """The bf16 path at value widths 32, 64, 96 (d_k = 128): one row (16-column chains) and eight
+    rows (32- or 64-column chains, 64 only where d_v is a multiple of 64), with the states path."""
+    import dataclasses
+    gdn = _lib()
+    w = dataclasses.replace(synth.WORKLOADS["prefill_t4096"], d_v=d_v)
+    inp = synth.make_inputs(w, seed=30 + d_v + B, T=150, B=B, s0_std=0.02)
+    d = to_dev(inp)
+    heads = [0, 31]
+    ref = _ref(inp, heads=heads, want_states=True)
+    full = _ref(inp)
+    o, fin = gdn.gdn_chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], initial_state=d["s0"])
+    o2, st, fin2 = gdn.gdn_states_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], initial_state=d["s0"])
+    torch.cuda.synchronize()
+    assert rel_max(host(o), full["o"]) <= TOL_BF16_O
+    assert rel_fro(host(fin), full["final"]) <= TOL_BF16_STATE
+    assert rel_max(host(o2), full["o"]) <= TOL_BF16_O
+    assert rel_fro(host(st[:, :, heads]), ref["states"]) <= TOL_BF16_STATE
+
+
 @pytest.mark.parametrize("B", [2, 4])
 def test_many_rows_both_paths(B):
     """Two or four rows of 32 heads: enough (row, head) pairs that the carry runs on 32-column
