@@ -168,8 +168,10 @@ def test_split_invariance_and_inplace_continuation():
     assert rel_fro(host(cache), host(fin_all)) <= 1e-5
 
 
-@pytest.mark.parametrize("H_qk,H_v", [(4, 4), (2, 6)])
+@pytest.mark.parametrize("H_qk,H_v", [(4, 4), (2, 6), (8, 8), (8, 24)])
 def test_other_head_ratios(H_qk, H_v):
+    """Head ratios 1 and 3 beside the 2 of the workloads; (8, 8) and (8, 24) also take the
+    prep kernel's XCD-aligned head order (query/key and value heads multiples of 8)."""
     gdn = _lib()
     w = synth.Workload("ratio", 2, 100, H_qk, H_v, 128, 128, 64, "bf16", 2.0, 0.02)
     inp = synth.make_inputs(w, seed=9)
