@@ -15,6 +15,17 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));  // raw 8-byte vecto
 
 constexpr int kWave = 64;
 
+// A raw buffer resource over `bytes` bytes at p (32-bit data format): buffer
+// stores at offsets past the end are dropped by the hardware.  The kernels mask
+// rows past a ragged end this way instead of with a branch: a branch around a
+// store leaves the compiler unable to count the outstanding vector-memory
+// operations past it (it then waits for all of them before the next load is
+// used), and a run of stores each behind its own exec-mask branch issues
+// measurably slower than the same stores unguarded.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(void *p, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(p, 0, (int)bytes, 0x00020000);
+}
+
 // ---------------------------------------------------------------------------
 // bf16 <-> f32.  Storage of bf16 data is uint16_t; conversions round to
 // nearest even (gfx950's v_cvt_pk_bf16_f32).

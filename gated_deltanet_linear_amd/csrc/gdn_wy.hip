@@ -107,16 +107,6 @@ __device__ __forceinline__ f32x2_t unpk_f16(uint32_t w) {
   return __builtin_convertvector(__builtin_bit_cast(f16x2_t, w), f32x2_t);
 }
 
-// A raw buffer resource over `bytes` bytes at p (32-bit data format): buffer
-// stores at offsets past the end are dropped by the hardware.  The chain masks
-// the rows past a ragged chunk's end this way instead of with a branch: a
-// branch around a store leaves the compiler unable to count the outstanding
-// vector-memory operations past it, and it then waits for all of them before
-// the next load is used.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(void *p, int64_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(p, 0, (int)bytes, 0x00020000);
-}
-
 // x = hi + lo + O(2^-17 |x|) for the 4 values of a (bf16).
 __device__ __forceinline__ void split4(const f32x4 &a, u32x2 &hi, u32x2 &lo) {
   const uint32_t h0 = pk_bf16(a[0], a[1]), h1 = pk_bf16(a[2], a[3]);
