@@ -18,9 +18,11 @@
 // The step is a pure HBM stream (0.74 FLOP per byte): one workgroup per
 // (b, h) of up to 1024 threads; each thread keeps a 4-column x (d_k / row
 // groups)-row strip of S in registers between the read and the write, so S
-// crosses HBM exactly twice.  Loads and stores are 16 bytes per lane and
-// non-temporal (the state is not reused before the next step), and each wave
-// instruction touches two whole 512-byte rows of S.
+// crosses HBM exactly twice.  Loads and stores are 16 bytes per lane, and each
+// wave instruction touches two whole 512-byte rows of S.  The loads are plain
+// and the stores non-temporal: on 256 sequences x 32 heads that pairing steps
+// ~9% faster than non-temporal loads and stores, and plain stores are slower
+// with either kind of load.
 #include "gdn_device.hpp"
 #include "gdn_internal.hpp"
 #include "gdn.h"
@@ -61,7 +63,7 @@ __global__ __launch_bounds__((StepCfg<DK, DV>::NT)) void step_kernel(
   f32x4 S[RPT];
 #pragma unroll
   for (int s = 0; s < RPT; ++s)
-    S[s] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(Sp + (int64_t)(rg + RG * s) * DV + 4 * cg));
+    S[s] = *reinterpret_cast<const f32x4 *>(Sp + (int64_t)(rg + RG * s) * DV + 4 * cg);
 
   const int64_t qk_off = ((int64_t)b * H_qk + j) * DK;
   for (int i = tid; i < DK; i += Cfg::NT) {
