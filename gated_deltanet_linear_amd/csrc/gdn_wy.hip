@@ -196,6 +196,30 @@ __global__ __launch_bounds__(256) void wy_prep_kernel(
   }
   const int tl = min(lane, len - 1);
   const float graw = g[(int64_t)(t0 + tl) * H_v + h], braw = beta[(int64_t)(t0 + tl) * H_v + h];
+  // 1/|q_r| (times the scale) and 1/|k_r| from the loaded rows: the 16 loads of
+  // row r sit on 16 neighbouring lanes, whose shuffle sum gives the row's sum of
+  // squares.  Rows past the length hold the last row (finite; their q, k rows
+  // are zero in LDS).
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float s2q = 0.f, s2k = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float q0 = bf_lo(qv[i][e]), q1 = bf_hi(qv[i][e]), k0 = bf_lo(kv[i][e]), k1 = bf_hi(kv[i][e]);
+      s2q += q0 * q0 + q1 * q1;
+      s2k += k0 * k0 + k1 * k1;
+    }
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) {
+      s2q += __shfl_xor(s2q, o);
+      s2k += __shfl_xor(s2k, o);
+    }
+    if ((lane & 15) == 0) {
+      const int r = (tid + 256 * i) >> 4;
+      sm.rq[r] = (l2norm ? 1.0f / sqrtf(s2q + 1e-6f) : 1.f) * scale;
+      sm.rk[r] = l2norm ? 1.0f / sqrtf(s2k + 1e-6f) : 1.f;
+    }
+  }
   const u32x4 zero = {0u, 0u, 0u, 0u};
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -212,21 +236,6 @@ __global__ __launch_bounds__(256) void wy_prep_kernel(
     sm.beta[lane] = lane < len ? braw : 0.f;
   }
   __syncthreads();
-  if (tid < 2 * C) {
-    const int r = tid % C;
-    float rn = 1.f;
-    if (l2norm) {
-      const uint16_t *row = (tid < C ? sq : sk) + r * LDQ;
-      float ss = 0.f;
-      for (int i = 0; i < DK; ++i) {
-        const float a = bf2f(row[i]);
-        ss += a * a;
-      }
-      rn = 1.0f / sqrtf(ss + 1e-6f);
-    }
-    if (tid < C) sm.rq[r] = rn * scale;
-    else sm.rk[r] = rn;
-  }
   // Gram tiles, 5 per wave, kept in registers: wave w takes the w + 1 tiles
   // (K Q^T)[16 ni.., 16 w..], ni <= w, whose accumulators hold P's rows of token
   // tile w (lane: row 16w + l%16, columns 16 ni + 4(l/16) + i), and 4 - w of the
