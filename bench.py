@@ -181,6 +181,116 @@ def bench_prefill(lib, b, synth, to_dev, steps, warmup):
     return w, ms, dict(zip(names, kern)), names[dom], flop, nbytes, cflop, cbytes
 
 
+def timed_launches(fn, iters, warmup, torch):
+    """Mean GPU time (ms) of `fn`, a bound C call that enqueues on the current stream,
+    over `iters` back-to-back calls between two events on that stream."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(iters):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / iters
+
+
+def bench_next_rows(lib, b, synth, to_dev, dev, torch, np):
+    """The widened rows: the 4096-token prefill at head ratios 1 (16/16) and 3 (16/48), the
+    mixer's output norm and input prologue at that prefill's shape, and the decode step with
+    the output norm fused, each with its roofline."""
+    import dataclasses
+    P = lambda t: ctypes.c_void_p(t.data_ptr() if t is not None else 0)
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    out = {}
+    base = synth.WORKLOADS["prefill_t4096"]
+    for H_v in (16, 48):
+        w = dataclasses.replace(base, H_v=H_v)
+        call = prepare_chunk(lib, b, to_dev(synth.make_inputs(w, seed=0)))
+        ms, kern = timed_chunk_calls(lib, [call], 10, 3, 3)
+        flop, nbytes, cflop, cbytes = chunk_work(w.T, H_v)
+        out[f"prefill_t4096_h16_{H_v}"] = {
+            "H_qk": 16, "H_v": H_v, "us_per_call": round(ms * 1e3, 2),
+            "tokens_per_s": round(w.T / (ms / 1e3), 1),
+            "kernel_us": {k: round(v * 1e3, 2) for k, v in zip(["plan", "prep", "carry"], kern)},
+            "roofline": roofline("mfma", cflop / (kern[2] / 1e3) / 1e12, MFMA_BF16_PEAK_TFLOPS, "TFLOP/s",
+                                 kernel="wy_chain_kernel")}
+        log(f"prefill 16/{H_v} heads: {ms * 1e3:.1f} us/call")
+        del call
+    # mixer steps at the prefill's shape (T = 4096, 16 qk / 32 v heads, d = 128)
+    w = base
+    mi = synth.make_mixer_inputs(w, seed=0)
+    bf = torch.bfloat16
+    x = torch.from_numpy(mi["x"]).to(dev, bf)
+    conv_w = torch.from_numpy(mi["conv_w"]).to(dev)
+    a = torch.from_numpy(mi["a"]).to(dev)
+    bb = torch.from_numpy(mi["b"]).to(dev)
+    A_log = torch.from_numpy(mi["A_log"]).to(dev)
+    dt_bias = torch.from_numpy(mi["dt_bias"]).to(dev)
+    z = torch.from_numpy(mi["z"]).to(dev, bf)
+    norm_w = torch.from_numpy(mi["norm_w"]).to(dev)
+    T, C = w.T, x.shape[2]
+    q = torch.empty((1, T, w.H_qk, w.d_k), dtype=bf, device=dev)
+    k = torch.empty_like(q)
+    v = torch.empty((1, T, w.H_v, w.d_v), dtype=bf, device=dev)
+    g = torch.empty((1, T, w.H_v), dtype=torch.float32, device=dev)
+    beta = torch.empty_like(g)
+    sp = b.GdnShape(1, T, w.H_qk, w.H_v, w.d_k, w.d_v, 1, 1.0, b.GDN_BF16, b.GDN_F32, 0)
+    pargs = [P(x), P(conv_w), P(None), P(None), P(a), P(bb), P(A_log), P(dt_bias), P(None), 0,
+             P(q), P(k), P(v), P(g), P(beta), stream]
+
+    def prologue():
+        if lib.gdn_mixer_prologue(ctypes.byref(sp), *pargs) != 0:
+            raise RuntimeError(lib.gdn_last_error().decode())
+    ms = timed_launches(prologue, 50, 5, torch)
+    pbytes = T * C * 2 + C * 4 * 4 + 2 * T * w.H_v * 4 + T * C * 2 + 2 * T * w.H_v * 4
+    out["prologue_t4096"] = {"us_per_call": round(ms * 1e3, 2),
+                             "roofline": roofline("hbm", pbytes / (ms / 1e3) / 1e9, HBM_PEAK_GBS, "GB/s",
+                                                  kernel="conv_silu_kernel + prologue_tail_kernel", algorithmic_bytes=pbytes)}
+    log(f"prologue: {ms * 1e3:.1f} us/call")
+    y = torch.randn((1, T, w.H_v, w.d_v), dtype=torch.float32, device=dev)
+    yo = torch.empty_like(y)
+    sn = b.GdnShape(1, T, 1, w.H_v, 1, w.d_v, 1, 1.0, b.GDN_BF16, b.GDN_F32, 0)
+    nargs = [P(y), P(z), P(norm_w), ctypes.c_float(1e-6), P(yo), stream]
+
+    def norm():
+        if lib.gdn_gated_norm(ctypes.byref(sn), *nargs) != 0:
+            raise RuntimeError(lib.gdn_last_error().decode())
+    ms = timed_launches(norm, 50, 5, torch)
+    nbytes = T * w.H_v * w.d_v * (4 + 2 + 4) + w.d_v * 4
+    out["gated_norm_t4096"] = {"us_per_call": round(ms * 1e3, 2),
+                               "roofline": roofline("hbm", nbytes / (ms / 1e3) / 1e9, HBM_PEAK_GBS, "GB/s",
+                                                    kernel="gated_norm_kernel", algorithmic_bytes=nbytes)}
+    log(f"gated norm: {ms * 1e3:.1f} us/call")
+    del x, conv_w, a, bb, z, q, k, v, g, beta, y, yo
+    # the decode step with the output norm fused (256 sequences, as the decode row)
+    wd = synth.WORKLOADS["decode_b256"]
+    pool = synth.make_decode_pool(wd, seed=0)
+    qd = torch.from_numpy(pool["q"][0]).to(dev, bf)
+    kd = torch.from_numpy(pool["k"][0]).to(dev, bf)
+    vd = torch.from_numpy(pool["v"][0]).to(dev, bf)
+    gd = torch.from_numpy(pool["g"][0]).to(dev)
+    bd = torch.from_numpy(pool["beta"][0]).to(dev)
+    state = torch.from_numpy(pool["s0"]).to(dev)
+    zd = torch.randn((wd.B, 1, wd.H_v, wd.d_v), device=dev).to(bf)
+    od = torch.empty((wd.B, 1, wd.H_v, wd.d_v), dtype=torch.float32, device=dev)
+    sd = b.GdnShape(wd.B, 1, wd.H_qk, wd.H_v, 128, 128, 64, 128 ** -0.5, b.GDN_BF16, b.GDN_F32, 0)
+    dargs = [P(qd), P(kd), P(vd), P(gd), P(bd), P(state), P(zd), P(norm_w), ctypes.c_float(1e-6), P(od), stream]
+
+    def gated_step():
+        if lib.gdn_recurrent_step_gated(ctypes.byref(sd), *dargs) != 0:
+            raise RuntimeError(lib.gdn_last_error().decode())
+    ms = timed_launches(gated_step, 200, 10, torch)
+    dbytes = 2 * wd.B * wd.H_v * 128 * 128 * 4 + wd.B * (2 * wd.H_qk * 128 * 2 + wd.H_v * 128 * 2 +
+                                                        2 * wd.H_v * 4 + wd.H_v * 128 * (4 + 2))
+    out["decode_gated_b256"] = {"us_per_step": round(ms * 1e3, 2),
+                                "roofline": roofline("hbm", dbytes / (ms / 1e3) / 1e9, HBM_PEAK_GBS, "GB/s",
+                                                     kernel="step_kernel (norm fused)", algorithmic_bytes=dbytes)}
+    log(f"decode step with the norm fused: {ms * 1e3:.1f} us/step")
+    return out
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -344,6 +454,8 @@ def main():
             "kernel_us": {k: round(v * 1e3, 2) for k, v in zip(["plan", "prep", "carry", "stream"], kx_)}}
         log(f"states, one per chunk: {msx * 1e3:.1f} us/call")
         del dsx, callx
+
+        result["next_rows"] = bench_next_rows(lib, b, synth, to_dev, dev, torch, np)
 
     # ---- the fp64 CPU oracle on the host, on the same workload -------------------------
     if not args.no_cpu:

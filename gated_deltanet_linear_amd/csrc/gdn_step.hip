@@ -78,6 +78,18 @@ __global__ __launch_bounds__((StepCfg<DK, DV>::NT)) void step_kernel(
     vv = f32x4{Elem<TIn>::get(v, vo), Elem<TIn>::get(v, vo + 1), Elem<TIn>::get(v, vo + 2),
                Elem<TIn>::get(v, vo + 3)};
   }
+  // The output norm's gate input and gain for this lane's 4 columns, loaded with
+  // the state so that their latency is not added at the end (every row group
+  // loads them; the lanes of row group 0 use them).
+  f32x4 zc = {0.f, 0.f, 0.f, 0.f}, wc = zc;
+  if constexpr (GN) {
+    const int64_t zo = (int64_t)bh * DV + 4 * cg;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      zc[c] = Elem<TIn>::get(z, zo + c);
+      wc[c] = wn[4 * cg + c];
+    }
+  }
   __syncthreads();
 
   // Norms and k.q (wave 0), shared through LDS.
@@ -155,12 +167,8 @@ __global__ __launch_bounds__((StepCfg<DK, DV>::NT)) void step_kernel(
 #pragma unroll
       for (int m = 1; m < CG; m <<= 1) ss += wave_xor(ss, m);
       const float rs = rsqrtf(ss * (1.0f / DV) + eps);
-      const int64_t zo = (int64_t)bh * DV + 4 * cg;
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const float zc = Elem<TIn>::get(z, zo + c);
-        out[c] = wn[4 * cg + c] * (out[c] * rs) * (zc / (1.0f + __expf(-zc)));
-      }
+      for (int c = 0; c < 4; ++c) out[c] = wc[c] * (out[c] * rs) * (zc[c] / (1.0f + __expf(-zc[c])));
     }
     if constexpr (OBF16) {
       uint16_t *op = reinterpret_cast<uint16_t *>(o) + (int64_t)bh * DV + 4 * cg;

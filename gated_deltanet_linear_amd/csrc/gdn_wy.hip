@@ -870,11 +870,11 @@ hipError_t run_wy(const Problem &p, const ChunkArgs &a, hipStream_t st) {
   }
   mark_event(a, 2, st);
   // Column blocks of 16, 32 or 64 columns: the width doubles while the narrower
-  // blocks would fill every CU twice over (wider blocks load each chunk's W,
-  // K^T and Q' once for more columns; narrower ones spread a few long chains
-  // over more CUs).
-  const int64_t chains16 = (int64_t)p.N * p.H_v * (p.d_v / 16), fill = 2 * (int64_t)device_cus();
-  const int nb = chains16 >= fill ? (p.d_v % 64 == 0 && chains16 / 2 >= fill ? 4 : 2) : 1;
+  // blocks would outnumber the CUs (wider blocks load each chunk's W, K^T and Q'
+  // once for more columns; narrower ones spread a few long chains over more
+  // CUs, but two of them sharing a CU each run slower than one wider block).
+  const int64_t chains16 = (int64_t)p.N * p.H_v * (p.d_v / 16), cus = (int64_t)device_cus();
+  const int nb = chains16 > cus ? (p.d_v % 64 == 0 && chains16 / 2 > cus ? 4 : 2) : 1;
   e = nb == 4 ? launch_chain<STATES, OBF16, 4>(p, a, sq, st)
       : nb == 2 ? launch_chain<STATES, OBF16, 2>(p, a, sq, st)
                 : launch_chain<STATES, OBF16, 1>(p, a, sq, st);
