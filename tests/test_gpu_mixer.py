@@ -140,6 +140,37 @@ def test_prologue_packed_with_state_in_place():
     np.testing.assert_array_equal(host(cs), r["conv_state"])
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_prologue_narrow_channel_layouts(dtype):
+    """Layouts off the 16-byte path: query/key width 4 (the q | k boundary is not a multiple of
+    8 channels) in bf16, and fp32 input, both 4 channels a thread; packed with an empty
+    sequence and a convolution state updated in place."""
+    import dataclasses
+    w = dataclasses.replace(W, H_qk=1, d_k=4, H_v=3, d_v=4, dtype=dtype)
+    lens = (5, 0, 17, 2)
+    mi = synth.make_mixer_inputs(w, seed=12, lengths=lens, with_conv_state=True)
+    state0 = mi["conv_state"].copy()
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    gdn = _gdn()
+    cs = _dev(state0)
+    q, k, v, g, beta, _ = gdn.gdn_mixer_prologue(
+        _dev(mi["x"], dt), _dev(mi["conv_w"]), _dev(mi["a"]), _dev(mi["b"]), _dev(mi["A_log"]),
+        _dev(mi["dt_bias"]), w.H_qk, w.d_k, w.H_v, w.d_v, conv_state=cs,
+        cu_seqlens=_dev(mi["cu_seqlens"], torch.int32), update_conv_state=True)
+    torch.cuda.synchronize()
+    r = mixer_ref.prologue(mi["x"][0], mi["conv_w"], mi["a"][0], mi["b"][0], mi["A_log"], mi["dt_bias"],
+                           w.H_qk, w.d_k, w.H_v, w.d_v, conv_state=state0, cu_seqlens=mi["cu_seqlens"])
+    for got, ref in ((q, r["q"]), (k, r["k"]), (v, r["v"])):
+        got = host(got)[0]
+        if dtype == "bf16":
+            assert _bf16_close(got, ref)
+        else:
+            assert rel_max(got, ref) <= 1e-5
+    assert rel_max(host(g)[0], r["g"]) <= 1e-5
+    assert rel_max(host(beta)[0], r["beta"]) <= 1e-5
+    np.testing.assert_array_equal(host(cs), r["conv_state"])
+
+
 def test_prologue_decode_steps_carry_the_state():
     """B rows of one token, the convolution state updated in place step after step, equal
     the whole sequences convolved at once."""
