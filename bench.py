@@ -64,6 +64,12 @@ def measured_traffic(kernel):
         return None
 
 
+def _sum_traffic(*kernels):
+    """Summed per-launch HBM bytes of kernels launched together, or None if any is unknown."""
+    parts = [measured_traffic(k) for k in kernels]
+    return None if any(x is None for x in parts) else sum(parts)
+
+
 class Prepared:
     """One chunked call with every pointer and the workspace bound once, so the timed
     loop issues the C call directly (no per-call tensor checks)."""
@@ -247,6 +253,7 @@ def bench_next_rows(lib, b, synth, to_dev, dev, torch, np):
     pbytes = T * C * 2 + C * 4 * 4 + 2 * T * w.H_v * 4 + T * C * 2 + 2 * T * w.H_v * 4
     out["prologue_t4096"] = {"us_per_call": round(ms * 1e3, 2),
                              "roofline": roofline("hbm", pbytes / (ms / 1e3) / 1e9, HBM_PEAK_GBS, "GB/s",
+                                                  traffic=_sum_traffic("conv_silu_kernel", "prologue_tail_kernel"),
                                                   kernel="conv_silu_kernel + prologue_tail_kernel", algorithmic_bytes=pbytes)}
     log(f"prologue: {ms * 1e3:.1f} us/call")
     y = torch.randn((1, T, w.H_v, w.d_v), dtype=torch.float32, device=dev)
@@ -261,6 +268,7 @@ def bench_next_rows(lib, b, synth, to_dev, dev, torch, np):
     nbytes = T * w.H_v * w.d_v * (4 + 2 + 4) + w.d_v * 4
     out["gated_norm_t4096"] = {"us_per_call": round(ms * 1e3, 2),
                                "roofline": roofline("hbm", nbytes / (ms / 1e3) / 1e9, HBM_PEAK_GBS, "GB/s",
+                                                    traffic=measured_traffic("gated_norm_kernel"),
                                                     kernel="gated_norm_kernel", algorithmic_bytes=nbytes)}
     log(f"gated norm: {ms * 1e3:.1f} us/call")
     del x, conv_w, a, bb, z, q, k, v, g, beta, y, yo
@@ -286,6 +294,7 @@ def bench_next_rows(lib, b, synth, to_dev, dev, torch, np):
                                                         2 * wd.H_v * 4 + wd.H_v * 128 * (4 + 2))
     out["decode_gated_b256"] = {"us_per_step": round(ms * 1e3, 2),
                                 "roofline": roofline("hbm", dbytes / (ms / 1e3) / 1e9, HBM_PEAK_GBS, "GB/s",
+                                                     traffic=measured_traffic("step_kernel_gated"),
                                                      kernel="step_kernel (norm fused)", algorithmic_bytes=dbytes)}
     log(f"decode step with the norm fused: {ms * 1e3:.1f} us/step")
     return out
