@@ -19,7 +19,7 @@ whose gain is its weight (the page's note "The readout is the plain
 projection": the DeltaNet's own output norm multiplies by its weight, every
 other RMS norm of the family by 1 + weight).
 
-Readings taken where the pages leave a step open (each is listed in the design doc):
+Readings taken where the pages leave a step open:
   * the norm is over one value head's d_v outputs, y / sqrt(mean(y^2) + eps),
     then times weight, then times silu(z): the gate multiplies the normalised
     output (the pages' norm(y, gate=...) with gain weight); eps = 1e-6, the
