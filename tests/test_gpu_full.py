@@ -42,6 +42,21 @@ def test_prefill_t4096(g_shift):
     _check_heads(o, fin, inp, [0, 13, 31])
 
 
+@pytest.mark.parametrize("H_v", [16, 48])
+def test_prefill_t4096_head_ratios(H_v):
+    """The 4096-token prefill at head ratios 1 (16/16: 128 column chains) and 3 (16/48: 32-column
+    chains, more blocks than CUs at 16 columns), as the benchmark times them."""
+    import dataclasses
+    gdn = _gdn()
+    w = dataclasses.replace(synth.WORKLOADS["prefill_t4096"], H_v=H_v)
+    inp = synth.make_inputs(w, seed=0)
+    d = to_dev(inp)
+    o, fin = gdn.gdn_chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"])
+    torch.cuda.synchronize()
+    assert torch.isfinite(o).all()
+    _check_heads(o, fin, inp, [0, H_v // 2 + 1, H_v - 1])
+
+
 def test_packed_8seq():
     gdn = _gdn()
     inp = synth.make_inputs(synth.WORKLOADS["packed_8seq"], seed=0)
