@@ -10,7 +10,7 @@ import torch
 
 from gated_deltanet_linear_amd import synth
 from oracle import gdn_ref
-from parity_util import TOL_BF16_O, TOL_BF16_STATE, host, rel_fro, rel_max, to_dev
+from parity_util import TOL_BF16_O, TOL_BF16_STATE, TOL_F32, host, rel_fro, rel_max, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -107,6 +107,39 @@ def test_decode_b256_1000_steps():
     eo = rel_max(o_gpu[:, :, 0], o_ref)
     print(f"o over {steps} steps: max|do|/rms = {eo:.3e}", flush=True)
     assert eo <= 1e-4
+
+
+def test_decode_gated_b256():
+    """The decode step with the output norm fused, at 256 sequences as the benchmark times it:
+    equal to the plain step followed by the norm, the state the same as the plain step's, and
+    the oracle (recurrence, then the norm) on sampled sequences over three steps."""
+    from oracle import mixer_ref
+    gdn = _gdn()
+    w = synth.WORKLOADS["decode_b256"]
+    pool = synth.make_decode_pool(w, seed=7, pool=3)
+    mi = synth.make_mixer_inputs(synth.WORKLOADS["prefill_t4096"], seed=7, T=3, B=w.B)
+    dev = lambda a, t=torch.float32: torch.from_numpy(np.ascontiguousarray(a)).to("cuda", t)
+    s_a = dev(pool["s0"])
+    s_b = s_a.clone()
+    wn = dev(mi["norm_w"])
+    rows = [0, 131, 255]
+    S = pool["s0"][rows]
+    for step in range(3):
+        q, k, v = (dev(pool[n][step], torch.bfloat16) for n in ("q", "k", "v"))
+        g, beta = dev(pool["g"][step]), dev(pool["beta"][step])
+        z = dev(mi["z"][:, step:step + 1], torch.bfloat16)
+        out = gdn.gdn_recurrent_step_gated(q, k, v, g, beta, s_a, z, wn, eps=1e-6)
+        o = gdn.gdn_recurrent_step(q, k, v, g, beta, s_b)
+        comp = gdn.gdn_gated_norm(o, z, wn, eps=1e-6)
+        torch.cuda.synchronize()
+        assert rel_max(host(out), host(comp)) <= 1e-5
+        assert torch.equal(s_a, s_b)
+        ref = gdn_ref.recurrent(*(pool[n][step][rows] for n in ("q", "k", "v", "g", "beta")), s0=S)
+        S = ref["final"].astype(np.float32)
+        want = mixer_ref.gated_rmsnorm(ref["o"], mi["z"][rows, step:step + 1], mi["norm_w"], eps=1e-6)
+        err = rel_max(host(out)[rows], want)
+        print(f"step {step}: fused output vs oracle on rows {rows}: {err:.3e}", flush=True)
+        assert err <= TOL_F32
 
 
 def test_states_t2048():
