@@ -556,6 +556,7 @@ template <int NB> struct StateOps {
 template <int NB> struct OutOps {
   u32x4 q[4];      // Q' (fp16) of token tile w, d_k steps 0..3
   f32x4 o[NB];     // O' tiles
+  uint32_t pf[2];  // words of the L2 warm-up loads (16-column chains), consumed a chunk later
 };
 
 template <bool STATES, bool OBF16, int NB>
@@ -771,6 +772,30 @@ __global__ __launch_bounds__(512) void wy_chain_kernel(
       for (int nb = 0; nb < NB; ++nb) op.o[nb] = O4[(w * NCT + jb * NB + nb) * 64 + lane];
     };
 
+    // L2 warm-up (16-column chains, which have a CU each): every chunk the output
+    // waves load one word of each 128-byte line this chain reads two chunks later
+    // (its 1/NCB share of the W, Q' and K^T lines all column blocks of its head
+    // read, its own U' and O' lines, the decay factors), so that those lines are
+    // in the XCD's L2 when the operand loads come.  The loaded words are consumed
+    // one chunk later, so no wait is added.
+    constexpr int kWarmAhead = 2;
+    const int ol = (wave - 4) * 64 + lane;
+    const int nS = 3 * 128 / NCB, nU = 32 * NB, nL = nS + 2 * nU + 4;
+    const int last_c = c_end - 1;
+    auto pf_ptr = [&](int cp, int L) -> const uint32_t * {
+      L = min(L, nL - 1);
+      const int ls = jb + NCB * min(L, nS - 1), reg = ls >> 7;
+      const unsigned char *ps = (reg == 0 ? wf + (hslot + cp) * kWyWBytes
+                                 : reg == 1 ? qf + (hslot + cp) * kWyQBytes
+                                            : ktf + (jslot + cp) * kWyKtBytes) + (ls & 127) * 128;
+      const int lu = min(max(L - nS, 0), 2 * nU - 1), x = lu % nU;
+      const float *ub = (lu < nU ? uf : of) + (hslot + cp) * (int64_t)(C * d_v);
+      const unsigned char *pu = reinterpret_cast<const unsigned char *>(ub) +
+                                (int64_t)((x / (8 * NB)) * NCT + jb * NB) * 1024 + (x % (8 * NB)) * 128;
+      const unsigned char *pfac = reinterpret_cast<const unsigned char *>(fac + (hslot + cp) * kWyFac) +
+                                  min(max(L - nS - 2 * nU, 0) * 128, 316);
+      return reinterpret_cast<const uint32_t *>(L < nS ? ps : L < nS + 2 * nU ? pu : pfac);
+    };
     auto chunk = [&](OutOps<NB> &op, int c, int cn) {
       const int t0 = s_begin + (c - c_begin) * C;
       const int len = min(C, s_end - t0);
@@ -791,6 +816,12 @@ __global__ __launch_bounds__(512) void wy_chain_kernel(
           else ao[nb] = mfma_f16(op.q[s], sv, ao[nb]);
         }
       load_out(op, cn);
+      if constexpr (NB == 1) {
+        asm volatile("" ::"v"(op.pf[0]), "v"(op.pf[1]));
+        const int cp = min(c + kWarmAhead, last_c);
+        op.pf[0] = *pf_ptr(cp, ol);
+        op.pf[1] = *pf_ptr(cp, ol + 256);
+      }
       {
         // rows t0 .. t0 + len of o (no row without o)
         const int esz = OBF16 ? 2 : 4;
@@ -818,6 +849,10 @@ __global__ __launch_bounds__(512) void wy_chain_kernel(
     if (c_begin < c_end) {
       OutOps<NB> op;
       load_out(op, c_begin);
+      if constexpr (NB == 1) {
+        op.pf[0] = *pf_ptr(min(c_begin + kWarmAhead, last_c), ol);
+        op.pf[1] = *pf_ptr(min(c_begin + kWarmAhead, last_c), ol + 256);
+      }
       // First chunk peeled, as on the state waves; past the last chunk the
       // loads repeat it and go unused.
       chunk(op, c_begin, min(c_begin + 1, c_end - 1));
