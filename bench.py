@@ -256,7 +256,7 @@ def bench_next_rows(lib, b, synth, to_dev, dev, torch, np):
                                                   traffic=_sum_traffic("conv_silu_kernel", "prologue_tail_kernel"),
                                                   kernel="conv_silu_kernel + prologue_tail_kernel", algorithmic_bytes=pbytes)}
     log(f"prologue: {ms * 1e3:.1f} us/call")
-    y = torch.randn((1, T, w.H_v, w.d_v), dtype=torch.float32, device=dev)
+    y = torch.from_numpy(np.random.default_rng(1).standard_normal((1, T, w.H_v, w.d_v), dtype=np.float32)).to(dev)
     yo = torch.empty_like(y)
     sn = b.GdnShape(1, T, 1, w.H_v, 1, w.d_v, 1, 1.0, b.GDN_BF16, b.GDN_F32, 0)
     nargs = [P(y), P(z), P(norm_w), ctypes.c_float(1e-6), P(yo), stream]
@@ -281,7 +281,7 @@ def bench_next_rows(lib, b, synth, to_dev, dev, torch, np):
     gd = torch.from_numpy(pool["g"][0]).to(dev)
     bd = torch.from_numpy(pool["beta"][0]).to(dev)
     state = torch.from_numpy(pool["s0"]).to(dev)
-    zd = torch.randn((wd.B, 1, wd.H_v, wd.d_v), device=dev).to(bf)
+    zd = torch.from_numpy(synth.make_mixer_inputs(base, seed=2, T=1, B=wd.B)["z"]).to(dev, bf)
     od = torch.empty((wd.B, 1, wd.H_v, wd.d_v), dtype=torch.float32, device=dev)
     sd = b.GdnShape(wd.B, 1, wd.H_qk, wd.H_v, 128, 128, 64, 128 ** -0.5, b.GDN_BF16, b.GDN_F32, 0)
     dargs = [P(qd), P(kd), P(vd), P(gd), P(bd), P(state), P(zd), P(norm_w), ctypes.c_float(1e-6), P(od), stream]
