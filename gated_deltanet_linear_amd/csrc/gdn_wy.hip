@@ -556,10 +556,10 @@ template <int NB> struct StateOps {
 template <int NB> struct OutOps {
   u32x4 q[4];      // Q' (fp16) of token tile w, d_k steps 0..3
   f32x4 o[NB];     // O' tiles
-  uint32_t pf[2];  // words of the L2 warm-up loads (16-column chains), consumed a chunk later
+  uint32_t pf[2];  // words of the L2 warm-up loads, consumed a chunk later
 };
 
-template <bool STATES, bool OBF16, int NB>
+template <bool STATES, bool OBF16, int NB, bool WARM>
 __global__ __launch_bounds__(512) void wy_chain_kernel(
     const float *__restrict__ s0, const Seqs sq, const unsigned char *__restrict__ wf,
     const unsigned char *__restrict__ qf, const float *__restrict__ uf, const float *__restrict__ of,
@@ -772,7 +772,7 @@ __global__ __launch_bounds__(512) void wy_chain_kernel(
       for (int nb = 0; nb < NB; ++nb) op.o[nb] = O4[(w * NCT + jb * NB + nb) * 64 + lane];
     };
 
-    // L2 warm-up (16-column chains, which have a CU each): every chunk the output
+    // L2 warm-up (WARM: 16-column chains that fill every CU): every chunk the output
     // waves load one word of each 128-byte line this chain reads two chunks later
     // (its 1/NCB share of the W, Q' and K^T lines all column blocks of its head
     // read, its own U' and O' lines, the decay factors), so that those lines are
@@ -816,7 +816,7 @@ __global__ __launch_bounds__(512) void wy_chain_kernel(
           else ao[nb] = mfma_f16(op.q[s], sv, ao[nb]);
         }
       load_out(op, cn);
-      if constexpr (NB == 1) {
+      if constexpr (WARM) {
         asm volatile("" ::"v"(op.pf[0]), "v"(op.pf[1]));
         const int cp = min(c + kWarmAhead, last_c);
         op.pf[0] = *pf_ptr(cp, ol);
@@ -849,7 +849,7 @@ __global__ __launch_bounds__(512) void wy_chain_kernel(
     if (c_begin < c_end) {
       OutOps<NB> op;
       load_out(op, c_begin);
-      if constexpr (NB == 1) {
+      if constexpr (WARM) {
         op.pf[0] = *pf_ptr(min(c_begin + kWarmAhead, last_c), ol);
         op.pf[1] = *pf_ptr(min(c_begin + kWarmAhead, last_c), ol + 256);
       }
@@ -880,9 +880,17 @@ hipError_t launch_chain(const Problem &p, const ChunkArgs &a, const Seqs &sq, hi
   const int groups = p.N * p.H_qk, ncb = p.d_v / (16 * NB);
   if (groups == 0 || ncb == 0) return hipSuccess;
   const int grid = xcd_group_grid(ncb * (p.H_v / p.H_qk), groups);
-  hipLaunchKernelGGL((wy_chain_kernel<STATES, OBF16, NB>), dim3(grid), dim3(512), 0, st, a.s0, sq, w.wf, w.qf,
-                     w.uf, w.of, w.fac, w.ktf, a.o, a.final_state, w.u, w.sc, p.H_qk, p.H_v, p.d_v,
-                     p.max_chunks, groups);
+  // The L2 warm-up pays where 16-column chains occupy every CU; with fewer
+  // chains than CUs (or wider blocks) it costs more than it saves.
+  const bool warm = NB == 1 && (int64_t)p.N * p.H_v * ncb >= device_cus();
+  if (warm)
+    hipLaunchKernelGGL((wy_chain_kernel<STATES, OBF16, NB, NB == 1>), dim3(grid), dim3(512), 0, st, a.s0, sq, w.wf,
+                       w.qf, w.uf, w.of, w.fac, w.ktf, a.o, a.final_state, w.u, w.sc, p.H_qk, p.H_v, p.d_v,
+                       p.max_chunks, groups);
+  else
+    hipLaunchKernelGGL((wy_chain_kernel<STATES, OBF16, NB, false>), dim3(grid), dim3(512), 0, st, a.s0, sq, w.wf,
+                       w.qf, w.uf, w.of, w.fac, w.ktf, a.o, a.final_state, w.u, w.sc, p.H_qk, p.H_v, p.d_v,
+                       p.max_chunks, groups);
   return hipGetLastError();
 }
 
