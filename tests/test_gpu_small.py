@@ -107,6 +107,44 @@ def test_packed_sequences_with_empty_ones():
     np.testing.assert_array_equal(host(fin)[5], inp["s0"][5])
 
 
+@pytest.mark.parametrize("case", ["beta0", "no_decay_full_write", "zero_q", "zero_k_l2norm"])
+def test_degenerate_regimes(case):
+    """The method's degenerate regimes against the oracle (150 tokens: two chunks and a ragged tail,
+    32 heads, initial state, kept fraction ~0.99 a token): beta = 0 (nothing written; the state only decays, to its closed form
+    e^{sum g} S0), g = 0 with beta = 1 (no decay, full delta writes), zero queries (o exactly 0) and
+    zero keys with the in-kernel l2 norm (normalised to 0: nothing written)."""
+    gdn = _lib()
+    inp = _bf16_case(T=150, seed=21, s0_std=0.02, g_shift=-5.0)  # slow decay: the state stays well above 0
+    l2 = False
+    if case == "beta0":
+        inp["beta"][:] = 0.0
+    elif case == "no_decay_full_write":
+        inp["g"][:] = 0.0
+        inp["beta"][:] = 1.0
+    elif case == "zero_q":
+        inp["q"][:] = 0.0
+    else:
+        inp["k"][:] = 0.0
+        l2 = True
+    d = to_dev(inp)
+    ref = _ref(inp, l2norm=l2)
+    o, fin = gdn.gdn_chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], initial_state=d["s0"], l2norm=l2)
+    o2, st, fin2 = gdn.gdn_states_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], initial_state=d["s0"],
+                                      l2norm=l2)
+    torch.cuda.synchronize()
+    if case == "zero_q":
+        assert float(o.abs().max()) == 0.0 and float(o2.abs().max()) == 0.0
+    else:
+        assert rel_max(host(o), ref["o"]) <= TOL_BF16_O
+        assert rel_max(host(o2), ref["o"]) <= TOL_BF16_O
+    assert rel_fro(host(fin), ref["final"]) <= TOL_BF16_STATE
+    assert rel_fro(host(st[:, -1]), ref["final"]) <= TOL_BF16_STATE
+    if case in ("beta0", "zero_k_l2norm"):
+        decay = np.exp(inp["g"].astype(np.float64).sum(axis=1))[0]          # [H_v]
+        closed = inp["s0"][0].astype(np.float64) * decay[:, None, None]
+        assert rel_fro(host(fin)[0], closed) <= 1e-5
+
+
 def test_minus_inf_resets_without_nan():
     gdn = _lib()
     inp = _bf16_case(T=150, seed=6, s0_std=0.02)
