@@ -145,6 +145,41 @@ def test_degenerate_regimes(case):
         assert rel_fro(host(fin)[0], closed) <= 1e-5
 
 
+@pytest.mark.parametrize("case", ["beta0", "no_decay_full_write", "zero_q", "zero_k_l2norm"])
+def test_decode_degenerate_regimes(case):
+    """The same regimes through the decode step: 4 rows of 32 heads, 5 consecutive in-place steps
+    against the oracle run over the same 5 tokens."""
+    gdn = _lib()
+    inp = _bf16_case(T=5, seed=22, s0_std=0.02, g_shift=-5.0, B=4)
+    l2 = False
+    if case == "beta0":
+        inp["beta"][:] = 0.0
+    elif case == "no_decay_full_write":
+        inp["g"][:] = 0.0
+        inp["beta"][:] = 1.0
+    elif case == "zero_q":
+        inp["q"][:] = 0.0
+    else:
+        inp["k"][:] = 0.0
+        l2 = True
+    d = to_dev(inp)
+    ref = _ref(inp, l2norm=l2)
+    state = d["s0"].clone()
+    outs = []
+    for t in range(5):
+        sl = slice(t, t + 1)
+        outs.append(gdn.gdn_recurrent_step(d["q"][:, sl].contiguous(), d["k"][:, sl].contiguous(),
+                                           d["v"][:, sl].contiguous(), d["g"][:, sl].contiguous(),
+                                           d["beta"][:, sl].contiguous(), state, l2norm=l2))
+    o = torch.cat(outs, dim=1)
+    torch.cuda.synchronize()
+    if case == "zero_q":
+        assert float(o.abs().max()) == 0.0
+    else:
+        assert rel_max(host(o), ref["o"]) <= TOL_F32
+    assert rel_max(host(state), ref["final"]) <= TOL_F32
+
+
 def test_minus_inf_resets_without_nan():
     gdn = _lib()
     inp = _bf16_case(T=150, seed=6, s0_std=0.02)
