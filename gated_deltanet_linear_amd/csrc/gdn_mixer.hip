@@ -11,6 +11,7 @@
 // consecutive channels.  The decode step fuses the epilogue into its own
 // kernel (gdn_step.hip); these kernels serve the prompt paths.
 #include <algorithm>
+#include <type_traits>
 
 #include "gdn_device.hpp"
 #include "gdn_internal.hpp"
@@ -101,6 +102,30 @@ struct SeqRows {
   __device__ __forceinline__ int seq_of(int t) const { return cu ? find_seq(cu, N, t) : t / rowT; }
 };
 
+// The 4 channels of T at p: their raw bytes (8 for bf16, 16 for fp32), and
+// unpacked to floats.
+template <typename T>
+using Raw4 = typename std::conditional<std::is_same<T, float>::value, u32x4, u32x2>::type;
+template <typename T> __device__ __forceinline__ Raw4<T> ld4raw(const T *p) {
+  return *reinterpret_cast<const Raw4<T> *>(p);
+}
+template <typename T> __device__ __forceinline__ void unpack4(const Raw4<T> &r, f32x4 &o) {
+  if constexpr (std::is_same<T, float>::value) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t u = r[e];  // (a bit cast of the vector element itself reads element 0)
+      o[e] = __builtin_bit_cast(float, u);
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const uint32_t u = r[e];
+      o[2 * e] = __builtin_bit_cast(float, u << 16);
+      o[2 * e + 1] = __builtin_bit_cast(float, u & 0xffff0000u);
+    }
+  }
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) void conv_silu_kernel(const T *__restrict__ x, const float *__restrict__ cw,
                                                         const float *__restrict__ cs_in, const SeqRows sr,
@@ -156,21 +181,35 @@ __global__ __launch_bounds__(256) void conv_silu_kernel(const T *__restrict__ x,
     int n = sr.seq_of(t0);
     int next = n + 1 < sr.N ? sr.start(n + 1) : sr.T_tot;
     reset(n, t0);
-    for (int t = t0; t < t1; ++t) {
-      if (t >= next) {  // a sequence starts here (skip the empty ones)
-        while (n + 1 < sr.N && sr.start(n + 1) <= t) ++n;
-        next = n + 1 < sr.N ? sr.start(n + 1) : sr.T_tot;
-        reset(n, t);
-      }
-      const f32x4 xt = load4(x + (int64_t)t * Cch + c);
-      f32x4 o;
+    // The next kAhead tokens' inputs are in flight while a token is computed and
+    // stored (raw bytes, unpacked at use; reads past the run repeat its last
+    // token and go unused).  Without them each token would wait for its own
+    // load and for the store before it.
+    constexpr int kAhead = 4;
+    Raw4<T> ring[kAhead];
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        o[j] = silu(wt[0][j] * h0[j] + wt[1][j] * h1[j] + wt[2][j] * h2[j] + wt[3][j] * xt[j]);
-      store4(dst + (int64_t)t * ld, o);
-      h0 = h1;
-      h1 = h2;
-      h2 = xt;
+    for (int i = 0; i < kAhead; ++i) ring[i] = ld4raw<T>(x + (int64_t)min(t0 + i, t1 - 1) * Cch + c);
+#pragma unroll
+    for (int i = 0; i < kRun; ++i) {
+      const int t = t0 + i;
+      if (t < t1) {
+        if (t >= next) {  // a sequence starts here (skip the empty ones)
+          while (n + 1 < sr.N && sr.start(n + 1) <= t) ++n;
+          next = n + 1 < sr.N ? sr.start(n + 1) : sr.T_tot;
+          reset(n, t);
+        }
+        f32x4 xt;
+        unpack4<T>(ring[i % kAhead], xt);
+        if (i + kAhead < kRun) ring[i % kAhead] = ld4raw<T>(x + (int64_t)min(t + kAhead, t1 - 1) * Cch + c);
+        f32x4 o;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          o[j] = silu(wt[0][j] * h0[j] + wt[1][j] * h1[j] + wt[2][j] * h2[j] + wt[3][j] * xt[j]);
+        store4(dst + (int64_t)t * ld, o);
+        h0 = h1;
+        h1 = h2;
+        h2 = xt;
+      }
     }
   }
 }
