@@ -86,7 +86,9 @@ hipError_t launch_norm_t(const Problem &p, const NormArgs &a, hipStream_t st) {
 // Thread (channel group of 4, run of kRun tokens): the three previous inputs
 // of its 4 channels ride along in registers, and are reset from the sequence's
 // convolution state (or zeros) wherever a sequence starts.  Consecutive
-// threads take consecutive channel groups of the same token.
+// threads take consecutive channel groups of the same token.  Unless the
+// convolution state is updated in place, the same launch also writes each
+// sequence's outgoing state (at its last token) and the gates.
 // ---------------------------------------------------------------------------
 constexpr int kRun = 16;
 
@@ -126,11 +128,34 @@ template <typename T> __device__ __forceinline__ void unpack4(const Raw4<T> &r, 
   }
 }
 
+// The gates of item r = (token, value head): g = -exp(A_log) softplus(a + dt_bias),
+// beta = sigmoid(b).
+__device__ __forceinline__ void gate_item(int64_t r, int H_v, const float *__restrict__ a,
+                                          const float *__restrict__ b, const float *__restrict__ A_log,
+                                          const float *__restrict__ dt_bias, float *__restrict__ g,
+                                          float *__restrict__ beta) {
+  const int h = (int)(r % H_v);
+  const float av = a[r] + dt_bias[h];
+  const float sp = av > 20.0f ? av : log1pf(__expf(av));  // softplus
+  g[r] = -__expf(A_log[h]) * sp;
+  beta[r] = 1.0f / (1.0f + __expf(-b[r]));
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) void conv_silu_kernel(const T *__restrict__ x, const float *__restrict__ cw,
                                                         const float *__restrict__ cs_in, const SeqRows sr,
                                                         int Cch, int nq, int nv, T *__restrict__ q,
-                                                        T *__restrict__ k, T *__restrict__ v) {
+                                                        T *__restrict__ k, T *__restrict__ v,
+                                                        float *__restrict__ cs_out, const float *__restrict__ a,
+                                                        const float *__restrict__ b, const float *__restrict__ A_log,
+                                                        const float *__restrict__ dt_bias, int H_v,
+                                                        float *__restrict__ g, float *__restrict__ beta) {
+  // Gates, when this launch carries them: one flat loop over every thread.
+  if (g) {
+    const int64_t n_gate = (int64_t)sr.T_tot * H_v, nthr = (int64_t)gridDim.x * gridDim.y * 256;
+    for (int64_t r = ((int64_t)blockIdx.y * gridDim.x + blockIdx.x) * 256 + threadIdx.x; r < n_gate; r += nthr)
+      gate_item(r, H_v, a, b, A_log, dt_bias, g, beta);
+  }
   const int g4 = blockIdx.x * 256 + threadIdx.x;
   const int c = 4 * g4;
   if (c >= Cch) return;
@@ -175,6 +200,17 @@ __global__ __launch_bounds__(256) void conv_silu_kernel(const T *__restrict__ x,
     h1 = hv[1];
     h2 = hv[2];
   };
+  // Outgoing state of an empty sequence: its incoming state (or zeros); the
+  // other sequences' states are written at their last token below.
+  if (cs_out && blockIdx.y == 0) {
+    for (int n = 0; n < sr.N; ++n) {
+      const int s = sr.start(n), e = n + 1 < sr.N ? sr.start(n + 1) : sr.T_tot;
+      if (e > s) continue;
+#pragma unroll
+      for (int i = 0; i < 12; ++i)
+        cs_out[((int64_t)n * Cch + c) * 3 + i] = cs_in ? cs_in[((int64_t)n * Cch + c) * 3 + i] : 0.0f;
+    }
+  }
   const int runs = (sr.T_tot + kRun - 1) / kRun;
   for (int run = blockIdx.y; run < runs; run += gridDim.y) {
     const int t0 = run * kRun, t1 = min(t0 + kRun, sr.T_tot);
@@ -209,14 +245,24 @@ __global__ __launch_bounds__(256) void conv_silu_kernel(const T *__restrict__ x,
         h0 = h1;
         h1 = h2;
         h2 = xt;
+        if (cs_out && t + 1 == next) {  // the sequence's last token: its last three inputs
+          float *so = cs_out + ((int64_t)n * Cch + c) * 3;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            so[3 * e] = h0[e];
+            so[3 * e + 1] = h1[e];
+            so[3 * e + 2] = h2[e];
+          }
+        }
       }
     }
   }
 }
 
-// Prologue, part 2 (after part 1, which reads the incoming states): each
-// sequence's outgoing convolution state, then the gates.  One flat loop over
-// N * Cch state items and T_tot * H_v gate items.
+// Prologue, part 2, for an in-place state update or no tokens (after part 1,
+// which reads the incoming states): each sequence's outgoing convolution state,
+// then the gates.  One flat loop over N * Cch state items and T_tot * H_v gate
+// items.
 template <typename T>
 __global__ __launch_bounds__(256) void prologue_tail_kernel(const T *__restrict__ x, const float *cs_in,
                                                             float *cs_out, const SeqRows sr, int Cch,
@@ -243,12 +289,7 @@ __global__ __launch_bounds__(256) void prologue_tail_kernel(const T *__restrict_
 #pragma unroll
       for (int j = 0; j < 3; ++j) cs_out[((int64_t)n * Cch + c) * 3 + j] = nv[j];  // after all reads
     } else {
-      const int64_t r = it - n_state;
-      const int h = (int)(r % H_v);
-      const float av = a[r] + dt_bias[h];
-      const float sp = av > 20.0f ? av : log1pf(__expf(av));  // softplus
-      g[r] = -__expf(A_log[h]) * sp;
-      beta[r] = 1.0f / (1.0f + __expf(-b[r]));
+      gate_item(it - n_state, H_v, a, b, A_log, dt_bias, g, beta);
     }
   }
 }
@@ -258,13 +299,19 @@ hipError_t launch_prologue_t(const Problem &p, const PrologueArgs &a, hipStream_
   const int nq = p.H_qk * p.d_k, nv = p.H_v * p.d_v, Cch = 2 * nq + nv;
   const SeqRows sr{a.cu, p.N, p.T, p.T_tot};
   const T *x = static_cast<const T *>(a.x);
+  // The convolution kernel also writes the outgoing states and the gates, except
+  // where the states are updated in place (every incoming state must be read
+  // before any is written: a second kernel does both then) or there are no tokens.
+  const bool fuse = p.T_tot > 0 && (a.cs_out == nullptr || a.cs_out != a.cs_in);
   if (p.T_tot > 0) {
     const int runs = (p.T_tot + kRun - 1) / kRun;
     const dim3 grid((unsigned)((Cch / 4 + 255) / 256), (unsigned)std::min(runs, 65535));
     hipLaunchKernelGGL((conv_silu_kernel<T>), grid, dim3(256), 0, st, x, a.conv_w, a.cs_in, sr, Cch, nq, nv,
-                       static_cast<T *>(a.q), static_cast<T *>(a.k), static_cast<T *>(a.v));
+                       static_cast<T *>(a.q), static_cast<T *>(a.k), static_cast<T *>(a.v),
+                       fuse ? a.cs_out : nullptr, a.a, a.b, a.A_log, a.dt_bias, p.H_v, fuse ? a.g : nullptr,
+                       a.beta);
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    if (e != hipSuccess || fuse) return e;
   }
   const int64_t items = (a.cs_out ? (int64_t)p.N * Cch : 0) + (int64_t)p.T_tot * p.H_v;
   if (items > 0) {

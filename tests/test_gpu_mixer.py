@@ -171,6 +171,65 @@ def test_prologue_narrow_channel_layouts(dtype):
     np.testing.assert_array_equal(host(cs), r["conv_state"])
 
 
+@pytest.mark.parametrize("dtype,narrow,lens,with_state", [
+    ("bf16", False, (70, 0, 1, 2, 130, 5), True),
+    ("bf16", False, (0, 33, 2, 0, 1), False),
+    ("fp32", True, (5, 0, 17, 2), True),
+    ("bf16", True, None, True),
+])
+def test_prologue_state_to_separate_buffer(dtype, narrow, lens, with_state):
+    """The outgoing convolution state written to its own buffer (the convolution kernel
+    writes it at each sequence's last token, and copies it for empty sequences), with and
+    without an incoming state, packed with empty and 1-2 token sequences, or dense rows;
+    the incoming state is left as it was."""
+    import dataclasses
+    w = dataclasses.replace(W, H_qk=1, d_k=4, H_v=3, d_v=4, dtype=dtype) if narrow else W
+    if lens is None:
+        mi = synth.make_mixer_inputs(w, seed=14, T=9, B=3, with_conv_state=with_state)
+    else:
+        mi = synth.make_mixer_inputs(w, seed=13, lengths=lens, with_conv_state=with_state)
+    state0 = mi["conv_state"].copy() if with_state else None
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    N = len(lens) if lens is not None else mi["x"].shape[0]
+    C = 2 * w.H_qk * w.d_k + w.H_v * w.d_v
+    gdn = _gdn()
+    cs_in = _dev(state0) if with_state else None
+    cs_out = torch.full((N, C, 3), float("nan"), dtype=torch.float32, device="cuda")
+    cu = None if lens is None else _dev(mi["cu_seqlens"], torch.int32)
+    q, k, v, g, beta, so = gdn.gdn_mixer_prologue(
+        _dev(mi["x"], dt), _dev(mi["conv_w"]), _dev(mi["a"]), _dev(mi["b"]), _dev(mi["A_log"]),
+        _dev(mi["dt_bias"]), w.H_qk, w.d_k, w.H_v, w.d_v, conv_state=cs_in, cu_seqlens=cu,
+        conv_state_out=cs_out)
+    torch.cuda.synchronize()
+    assert so.data_ptr() == cs_out.data_ptr()
+    refs = []
+    if lens is None:
+        for b in range(N):
+            refs.append(mixer_ref.prologue(mi["x"][b], mi["conv_w"], mi["a"][b], mi["b"][b], mi["A_log"],
+                                           mi["dt_bias"], w.H_qk, w.d_k, w.H_v, w.d_v,
+                                           conv_state=None if state0 is None else state0[b:b + 1]))
+        ref_state = np.concatenate([r["conv_state"] for r in refs])
+        got_rows = [(host(t), [r[key] for r in refs]) for t, key in ((q, "q"), (k, "k"), (v, "v"))]
+        for got, ref in got_rows:
+            for b in range(N):
+                assert (_bf16_close(got[b], ref[b]) if dtype == "bf16" else rel_max(got[b], ref[b]) <= 1e-5)
+        for b in range(N):
+            assert rel_max(host(g)[b], refs[b]["g"]) <= 1e-5
+            assert rel_max(host(beta)[b], refs[b]["beta"]) <= 1e-5
+    else:
+        r = mixer_ref.prologue(mi["x"][0], mi["conv_w"], mi["a"][0], mi["b"][0], mi["A_log"], mi["dt_bias"],
+                               w.H_qk, w.d_k, w.H_v, w.d_v, conv_state=state0, cu_seqlens=mi["cu_seqlens"])
+        ref_state = r["conv_state"]
+        for got, ref in ((q, r["q"]), (k, r["k"]), (v, r["v"])):
+            got = host(got)[0]
+            assert (_bf16_close(got, ref) if dtype == "bf16" else rel_max(got, ref) <= 1e-5)
+        assert rel_max(host(g)[0], r["g"]) <= 1e-5
+        assert rel_max(host(beta)[0], r["beta"]) <= 1e-5
+    np.testing.assert_array_equal(host(cs_out), ref_state)
+    if with_state:
+        np.testing.assert_array_equal(host(cs_in), state0)
+
+
 def test_prologue_decode_steps_carry_the_state():
     """B rows of one token, the convolution state updated in place step after step, equal
     the whole sequences convolved at once."""
