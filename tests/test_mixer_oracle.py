@@ -1,8 +1,9 @@
 """Pins of the mixer references (oracle/mixer_ref.py) against values worked by hand and
 against library routines, not against the references themselves.  CPU only.
 
-- gated RMS norm: a hand-worked example whose values are exact multiples of ln 3
-  (tests/golden/gated_norm_d4.json), scale invariance, a zero row;
+- gated RMS norm: hand-worked examples whose values are exact multiples of ln 3, with
+  eps = 0 (tests/golden/gated_norm_d4.json) and with an eps of the order of each row's
+  mean square (tests/golden/gated_norm_eps_d4.json), scale invariance, a zero row;
 - causal convolution: impulse response (the filter reversed, nothing before the
   impulse), numpy.convolve per channel, split invariance through the carried state,
   restart at every packed sequence;
@@ -27,6 +28,18 @@ def test_gated_norm_hand_worked():
     y = mixer_ref.gated_rmsnorm(np.array(fx["y"], float), z, np.array(fx["weight"], float), eps=0.0)
     want = np.array([c * ln3 for c in fx["out_in_ln3"]])
     np.testing.assert_allclose(y, want, rtol=1e-14, atol=1e-14)
+
+
+def test_gated_norm_hand_worked_with_eps():
+    # eps sits inside the square root, added to the mean square: rows whose mean square
+    # is comparable to eps pin both its place and its value
+    with open(os.path.join(GOLDEN, "gated_norm_eps_d4.json")) as f:
+        fx = json.load(f)
+    ln3 = math.log(3.0)
+    z = np.array(fx["z_in_ln3"], float) * ln3
+    y = mixer_ref.gated_rmsnorm(np.array(fx["y"], float), z, np.array(fx["weight"], float), eps=fx["eps"])
+    want = np.array(fx["out_in_ln3"], float) * ln3
+    np.testing.assert_allclose(y, want, rtol=1e-12, atol=1e-15)
 
 
 def test_gated_norm_scale_invariance_and_zero_row():
