@@ -257,7 +257,7 @@ __global__ __launch_bounds__(256) void prep_kernel(
       double gv = 0.0;
       float bv = 0.f;
       if (lane < len) {
-        gv = (double)fmaxf(g[(int64_t)(t0 + lane) * H_v + h], kGFloor);
+        gv = (double)floor_keep_nan(g[(int64_t)(t0 + lane) * H_v + h], kGFloor);
         bv = beta[(int64_t)(t0 + lane) * H_v + h];
       }
       const double gam = wave_inclusive_scan(gv, lane);

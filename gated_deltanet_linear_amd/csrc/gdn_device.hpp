@@ -178,6 +178,11 @@ __device__ __forceinline__ int xcd_group_remap(int bid, int per, int groups) {
 }
 inline int xcd_group_grid(int per, int groups) { return (groups + 7) / 8 * 8 * per; }
 
+// max(x, lo) that keeps a NaN a NaN (fmaxf would return lo): the decay floor turns
+// g = -inf into a finite reset, while a NaN decay propagates as it does through the
+// oracle, the decode step and the states stream.
+__device__ __forceinline__ float floor_keep_nan(float x, float lo) { return x < lo ? lo : x; }
+
 // Non-temporal 16-byte store (streamed output that is not read back soon).
 __device__ __forceinline__ void store_nt(float4 *p, const float4 &v) {
   __builtin_nontemporal_store(v.x, &p->x);

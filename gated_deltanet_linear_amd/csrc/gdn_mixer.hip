@@ -1,10 +1,12 @@
 // The DeltaNet mixer's steps around the delta rule (Qwen3.5 text encyclopedia
-// page, note "The DeltaNet mixer"; Qwen3-Next encyclopedia page, same note):
+// page, note "The DeltaNet mixer"; Qwen3-Next encyclopedia page, same note),
+// in this library's notation, for channel c, token t and value head h:
 //
-//   prologue:  q, k, v = split(silu(conv1d(x)))    causal, width 4, depthwise
-//              beta    = sigmoid(b)
-//              g       = -exp(A_log) * softplus(a + dt_bias)
-//   epilogue:  out     = norm(y, gate = silu(z))   gain weight, per value head
+//   prologue:  xc[t,c]  = sum_{i<4} w[c,i] x[t-3+i,c]  (causal, one filter per channel)
+//              (q|k|v)[t,c] = xc[t,c] sigma(xc[t,c])    channels split q, then k, then v
+//              beta[t,h] = sigma(b[t,h]),  g[t,h] = -e^{A_log[h]} ln(1 + e^{a[t,h] + dt_bias[h]})
+//   epilogue:  out[t,h,:] = weight * y / sqrt(mean(y^2) + eps) * z sigma(z)
+//                           over one value head's d_v outputs y = y[t,h,:], z = z[t,h,:]
 //
 // All three are elementwise or nearly so, bound by HBM: one pass over their
 // inputs and outputs, 16-byte (fp32) or 8-byte (bf16) accesses per lane on

@@ -229,7 +229,7 @@ __global__ __launch_bounds__(256) void wy_prep_kernel(
   }
   // In-chunk cumulative decay (fp64) and write strengths; zero past the length.
   if (w == 3) {
-    const double gv = lane < len ? (double)fmaxf(graw, kFloor) : 0.0;
+    const double gv = lane < len ? (double)floor_keep_nan(graw, kFloor) : 0.0;
     const double gm = wave_inclusive_scan(gv, lane);
     sm.gam[lane] = gm;
     sm.eg[lane] = fexp((float)gm);

@@ -189,13 +189,15 @@ gdn_status gdn_states_fwd_strided(const gdn_shape *s, const void *q, const void 
 
 /*
  * The mixer's steps around the delta rule (Qwen3.5 text encyclopedia page,
- * note "The DeltaNet mixer"; Qwen3-Next encyclopedia page, same note):
+ * note "The DeltaNet mixer"; Qwen3-Next encyclopedia page, same note), for
+ * channel c, token t and value head h, sigma the logistic function:
  *
- *     q, k, v = split(silu(conv1d(x)))       causal, width 4, one filter per channel
- *     beta    = sigmoid(b)
- *     g       = -exp(A_log) * softplus(a + dt_bias)
- *     y, S    = delta_rule(...)                (the entry points above)
- *     out     = norm(y, gate = silu(z))        gain weight
+ *   before:  xc[t,c] = sum_{i<4} w[c,i] x[t-3+i,c], causal and one filter per
+ *            channel; q, k, v are xc sigma(xc) on the q, k and v channels;
+ *            beta = sigma(b); g = -e^{A_log} ln(1 + e^{a + dt_bias})
+ *   kernel:  the gated delta rule above on q, k, v, g, beta
+ *   after:   out[t,h,:] = weight * y / sqrt(mean(y^2) + eps) * z sigma(z), over
+ *            the d_v outputs y of one value head and its gate input z
  *
  * The module listing on the first page gives the convolution as depthwise, kernel
  * size 4, padding 3, no bias; the note "The readout is the plain projection"

@@ -5,13 +5,19 @@ benchmark's ``cpu_baseline`` leg may import this module.  The HIP product path
 never imports it and shares no code with it.
 
 The Qwen3.5 text encyclopedia page (note "The DeltaNet mixer") and the
-Qwen3-Next encyclopedia page (same note) state the mixer around the kernel as
+Qwen3-Next encyclopedia page (same note) describe the mixer around the kernel;
+restated here for channel c, token t and value head h, sigma the logistic
+function:
 
-    q, k, v = split(silu(conv1d(x_qkv)))     causal, width 4, one filter per channel
-    beta    = sigmoid(b)
-    g       = -exp(A_log) * softplus(a + dt_bias)
-    y, S    = delta_rule(l2norm(q) / sqrt(128), l2norm(k), v, g, beta)
-    out     = out_proj(norm(y, gate=silu(z)))        gain: weight
+  * a causal convolution of width 4 with one filter per channel,
+    xc[t,c] = sum_{i<4} w[c,i] x[t-3+i,c], then SiLU, xc sigma(xc), and a split of
+    the channels into q, k and v;
+  * the write strength beta = sigma(b) and the log decay
+    g = -e^{A_log[h]} softplus(a[t,h] + dt_bias[h]);
+  * the gated delta rule on the l2-normed q times d_k^{-1/2}, the l2-normed k, v,
+    g and beta;
+  * on each value head's output y[t,h,:], an RMS norm with gain weight, multiplied
+    by the SiLU of the gate input z[t,h,:], before the output projection.
 
 and the module listing on the first page shows the convolution as a depthwise
 Conv1d of kernel size 4 with padding 3 and no bias, and the norm as an RMS norm
