@@ -15,7 +15,9 @@ from typing import Optional
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-library_path = os.path.join(_PKG, "libgdn.so")
+# GDN_LIBRARY names another build of the same ABI (the host-sanitized copy of
+# `python -m gated_deltanet_linear_amd.build --sanitize`, for CPU runs of the ABI tests).
+library_path = os.environ.get("GDN_LIBRARY") or os.path.join(_PKG, "libgdn.so")
 
 GDN_F32, GDN_BF16 = 0, 1
 GDN_QK_L2NORM = 1
