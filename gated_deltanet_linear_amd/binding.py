@@ -123,7 +123,7 @@ def _shape(q, v, chunk, scale, l2norm, o_dtype, B, T):
     if o_dtype not in _DT:
         raise ValueError(f"o_dtype {o_dtype} is not float32 or bfloat16")
     if chunk is None:
-        chunk = 64 if q.dtype == torch.bfloat16 else 16
+        chunk = 16 if q.shape[-1] == 16 else 64
     if scale is None:
         scale = d_k ** -0.5
     s = GdnShape(B, T, H_qk, H_v, d_k, d_v, chunk, float(scale), _DT[q.dtype], _DT[o_dtype],

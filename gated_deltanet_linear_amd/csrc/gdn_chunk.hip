@@ -906,8 +906,14 @@ static hipError_t stream_rows(const Problem &p, const ChunkArgs &a, const Seqs &
 }
 
 hipError_t launch_states_stream(const Problem &p, const ChunkArgs &a, const Seqs &sq, hipStream_t st) {
-  if (p.dtype == GDN_BF16 && p.C == 64) return stream_rows<uint16_t, 64>(p, a, sq, st);
-  if (p.dtype == GDN_F32 && p.C == 16) return stream_rows<float, 16>(p, a, sq, st);
+  if (p.dtype == GDN_BF16) {
+    if (p.C == 64) return stream_rows<uint16_t, 64>(p, a, sq, st);
+    if (p.C == 32) return stream_rows<uint16_t, 32>(p, a, sq, st);
+  } else {
+    if (p.C == 64) return stream_rows<float, 64>(p, a, sq, st);
+    if (p.C == 32) return stream_rows<float, 32>(p, a, sq, st);
+    if (p.C == 16) return stream_rows<float, 16>(p, a, sq, st);
+  }
   return hipErrorInvalidValue;
 }
 
@@ -955,14 +961,37 @@ static hipError_t run_cfg(const Problem &p, const ChunkArgs &a, bool states, hip
 
 bool chunk_path_supported(const Problem &p) {
   // d_v <= 128 keeps the states stream's LDS staging (C x d_v fp32) within 64 KiB.
-  if (p.dtype == GDN_BF16) return p.d_k == 128 && p.C == 64 && p.d_v % 32 == 0 && p.d_v <= 128;
-  return p.d_k == 16 && p.C == 16 && p.d_v % 16 == 0 && p.d_v <= 128;
+  if (p.d_v > 128) return false;
+  if (p.dtype == GDN_BF16) {
+    if (p.d_k != 128) return false;  // bf16 MFMA contracts over 32: d_k and C multiples of 32
+    if (p.C == 64) return p.d_v % 32 == 0;
+    return p.C == 32 && p.d_v % 16 == 0;
+  }
+  return (p.d_k == 16 || p.d_k == 128) && (p.C == 16 || p.C == 32 || p.C == 64) && p.d_v % 16 == 0;
+}
+
+// fp32 inputs at every supported (d_k, chunk), and bf16 inputs at chunk 32, take the
+// general path of this file (fp32: exact fp32 MFMA; bf16: hi/lo bf16 operands); bf16
+// at chunk 64 takes the W/U' path of gdn_wy.hip.
+template <typename TIn, int DK>
+static hipError_t run_chunk(const Problem &p, const ChunkArgs &a, bool states, hipStream_t st) {
+  if constexpr (std::is_same<TIn, float>::value) {
+    if (p.C == 16) return run_cfg<TIn, DK, 16, 16>(p, a, states, st);
+  }
+  if (p.C == 32) return run_cfg<TIn, DK, 32, 16>(p, a, states, st);
+  if constexpr (std::is_same<TIn, float>::value) {
+    if (p.C == 64) return run_cfg<TIn, DK, 64, 16>(p, a, states, st);
+  }
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_chunk_path(const Problem &p, const ChunkArgs &a, bool states, hipStream_t st) {
-  if (p.dtype == GDN_BF16 && p.d_k == 128 && p.C == 64) return launch_wy_path(p, a, states, st);
-  if (p.dtype == GDN_F32 && p.d_k == 16 && p.C == 16) return run_cfg<float, 16, 16, 16>(p, a, states, st);
-  return hipErrorInvalidValue;
+  if (!chunk_path_supported(p)) return hipErrorInvalidValue;
+  if (p.dtype == GDN_BF16) {
+    if (p.C == 64) return launch_wy_path(p, a, states, st);
+    return run_chunk<uint16_t, 128>(p, a, states, st);
+  }
+  return p.d_k == 16 ? run_chunk<float, 16>(p, a, states, st) : run_chunk<float, 128>(p, a, states, st);
 }
 
 Workspace workspace_layout(const Problem &p, bool states, void *base) {
@@ -977,7 +1006,7 @@ Workspace workspace_layout(const Problem &p, bool states, void *base) {
   const size_t ss = take(sizeof(int32_t) * ((size_t)p.N + 1));
   const size_t cf = take(sizeof(int32_t) * ((size_t)p.N + 1));
   const size_t cc = (size_t)p.max_chunks * p.H_v;
-  const bool wy = p.dtype == GDN_BF16;
+  const bool wy = p.dtype == GDN_BF16 && p.C == 64;  // the W/U' path of gdn_wy.hip
   size_t tb = 0, pm = 0, eg = 0, eb = 0, wf = 0, qf = 0, uf = 0, of = 0, fc = 0, kt = 0;
   if (wy) {
     wf = take(kWyWBytes * cc);

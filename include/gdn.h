@@ -84,7 +84,10 @@ typedef struct {
 /*
  * Built kernel set (anything else returns GDN_ERR_UNSUPPORTED):
  *   chunked paths:  dtype GDN_BF16 with d_k = 128, chunk = 64, d_v in {32, 64, 96, 128};
- *                   dtype GDN_F32  with d_k = 16,  chunk = 16, d_v in {16, 32, ..., 128}.
+ *                   dtype GDN_BF16 with d_k = 128, chunk = 32, d_v in {16, 32, ..., 128};
+ *                   dtype GDN_F32  with d_k in {16, 128}, chunk in {16, 32, 64},
+ *                                  d_v in {16, 32, ..., 128}.
+ *                   (bf16 MFMA contracts over 32 elements: bf16 needs d_k = 128.)
  *   decode step:    d_k in {16, 128}, d_v in {16, 128}, either dtype.
  */
 
