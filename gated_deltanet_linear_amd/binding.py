@@ -38,7 +38,7 @@ class GdnShape(ctypes.Structure):
                 ("o_dtype", ctypes.c_int32), ("flags", ctypes.c_uint32)]
 
 
-EXPORTS = ("gdn_chunk_fwd", "gdn_chunk_fwd_workspace", "gdn_recurrent_step", "gdn_states_fwd",
+EXPORTS = ("gdn_chunk_fwd", "gdn_chunk_fwd_workspace", "gdn_chunk_fwd_noalloc", "gdn_recurrent_step", "gdn_states_fwd",
            "gdn_states_fwd_strided", "gdn_states_fwd_workspace", "gdn_gated_norm", "gdn_recurrent_step_gated",
            "gdn_mixer_prologue", "gdn_set_timing_events", "gdn_status_string",
            "gdn_last_error", "gdn_version")
@@ -61,6 +61,8 @@ def load_library(path: Optional[str] = None):
     lib.gdn_chunk_fwd.argtypes = [S, P, P, P, P, P, P, P, I, P, P, P, Z, P]
     lib.gdn_chunk_fwd_workspace.restype = Z
     lib.gdn_chunk_fwd_workspace.argtypes = [S, I]
+    lib.gdn_chunk_fwd_noalloc.restype = ctypes.c_int
+    lib.gdn_chunk_fwd_noalloc.argtypes = [S, P, P, P, P, P, P, P, I, P, P, P]
     lib.gdn_states_fwd.restype = ctypes.c_int
     lib.gdn_states_fwd.argtypes = [S, P, P, P, P, P, P, P, I, P, P, P, P, Z, P]
     lib.gdn_states_fwd_strided.restype = ctypes.c_int
@@ -190,6 +192,30 @@ def gdn_chunk_fwd(q, k, v, g, beta, initial_state=None, cu_seqlens=None, scale=N
                            _ptr(initial_state), _ptr(cu_seqlens), nseq, _ptr(o), _ptr(final_state),
                            _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(dev))
     _check(lib, st, "gdn_chunk_fwd")
+    return o, final_state
+
+
+def gdn_chunk_fwd_noalloc(q, k, v, g, beta, initial_state=None, cu_seqlens=None, scale=None, chunk=None,
+                          l2norm=False, o_dtype=torch.float32, output_final_state=True, o=None,
+                          final_state=None):
+    """gdn_chunk_fwd through the entry point that allocates nothing (its workspace is the
+    library's static device scratch).  Pass o and final_state to allocate nothing here
+    either.  Returns (o, final_state or None)."""
+    lib = load_library()
+    dev, B, T, H_qk, H_v, d_k, d_v, N = _common(q, k, v, g, beta, initial_state, cu_seqlens)
+    s = _shape(q, v, chunk, scale, l2norm, o_dtype, B, T)
+    if o is None:
+        o = torch.empty((B, T, H_v, d_v), dtype=o_dtype, device=dev)
+    _need(o, "o", (B, T, H_v, d_v), o_dtype, dev)
+    if output_final_state and final_state is None:
+        final_state = torch.empty((N, H_v, d_k, d_v), dtype=torch.float32, device=dev)
+    if final_state is not None:
+        _need(final_state, "final_state", (N, H_v, d_k, d_v), torch.float32, dev)
+    nseq = N if cu_seqlens is not None else 0
+    st = lib.gdn_chunk_fwd_noalloc(ctypes.byref(s), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                   _ptr(initial_state), _ptr(cu_seqlens), nseq, _ptr(o), _ptr(final_state),
+                                   _stream(dev))
+    _check(lib, st, "gdn_chunk_fwd_noalloc")
     return o, final_state
 
 

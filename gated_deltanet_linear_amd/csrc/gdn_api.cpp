@@ -12,6 +12,8 @@
 #include "gdn.h"
 #include "gdn_internal.hpp"
 
+static_assert(GDN_NOALLOC_SCRATCH_BYTES == gdn::kNoAllocScratchBytes, "the header states the static scratch size");
+
 namespace {
 
 thread_local std::string g_last_error;
@@ -259,6 +261,31 @@ gdn_status gdn_chunk_fwd(const gdn_shape *s, const void *q, const void *k, const
   try {
     return chunked_common(s, q, k, v, g, beta, initial_state, cu_seqlens, num_seqs, o, nullptr, final_state,
                           workspace, workspace_bytes, stream, false);
+  } catch (const std::exception &e) {
+    return fail(GDN_ERR_HIP, "internal error: %s", e.what());
+  } catch (...) {
+    return fail(GDN_ERR_HIP, "internal error");
+  }
+}
+
+gdn_status gdn_chunk_fwd_noalloc(const gdn_shape *s, const void *q, const void *k, const void *v, const float *g,
+                                 const float *beta, const float *initial_state, const int32_t *cu_seqlens,
+                                 int32_t num_seqs, void *o, float *final_state, hipStream_t stream) {
+  try {
+    gdn::Problem p;
+    gdn_status st = check_shape(s, cu_seqlens != nullptr, num_seqs, 0, p);
+    if (st != GDN_OK) return st;
+    const size_t need = gdn::workspace_layout(p, false, nullptr).bytes;
+    if (need > gdn::kNoAllocScratchBytes)
+      return fail(GDN_ERR_WORKSPACE,
+                  "this call needs %zu bytes of scratch; gdn_chunk_fwd_noalloc's static scratch holds %zu "
+                  "(GDN_NOALLOC_SCRATCH_BYTES): use gdn_chunk_fwd with a workspace",
+                  need, gdn::kNoAllocScratchBytes);
+    void *ws = nullptr;
+    const hipError_t e = gdn::noalloc_scratch(&ws);
+    if (e != hipSuccess) return fail(GDN_ERR_HIP, "static scratch lookup failed: %s", hipGetErrorString(e));
+    return chunked_common(s, q, k, v, g, beta, initial_state, cu_seqlens, num_seqs, o, nullptr, final_state, ws,
+                          gdn::kNoAllocScratchBytes, stream, false);
   } catch (const std::exception &e) {
     return fail(GDN_ERR_HIP, "internal error: %s", e.what());
   } catch (...) {

@@ -58,6 +58,12 @@ struct Workspace {
 constexpr size_t kWyWBytes = 16384, kWyQBytes = 16384, kWyKtBytes = 16384;
 constexpr int kWyFac = 80;
 
+// Size of the static device scratch that gdn_chunk_fwd_noalloc uses as its workspace
+// (gdn_noalloc.hip), and its device address on the current device (looked up once
+// per device; the array's host-side name is never passed to a kernel).
+constexpr size_t kNoAllocScratchBytes = (size_t)64 << 20;
+hipError_t noalloc_scratch(void **ptr);
+
 // Computes the layout; with base == nullptr only `bytes` is meaningful.
 Workspace workspace_layout(const Problem &p, bool states, void *base);
 

@@ -127,6 +127,33 @@ gdn_status gdn_chunk_fwd(const gdn_shape *s, const void *q, const void *k,
 size_t gdn_chunk_fwd_workspace(const gdn_shape *s, int32_t num_seqs);
 
 /*
+ * gdn_chunk_fwd_noalloc: gdn_chunk_fwd for callers that cannot allocate device
+ * memory -- code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  It takes no workspace: its kernels use a static device array
+ * of GDN_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it runs on
+ * until the process ends, and the call allocates nothing (no hipMalloc, no
+ * allocating library routine).  The caller still passes every input and output,
+ * as for gdn_chunk_fwd, with the same meaning, layout and ownership.
+ *
+ *   Limit: a shape whose gdn_chunk_fwd_workspace() exceeds
+ *          GDN_NOALLOC_SCRATCH_BYTES returns GDN_ERR_WORKSPACE and writes nothing.
+ *   Sharing: every call on one GPU uses that GPU's one array, which keeps the
+ *          last call's contents; calls that overlap in time on one GPU (two
+ *          streams, two threads) race and must be serialised by the caller.
+ *   Status: a bad cu_seqlens array sets the status word at the start of the
+ *          static array (not readable through this ABI); the kernels then do
+ *          nothing, as in gdn_chunk_fwd.
+ *   The first call on a device looks the array's address up once (a host-side
+ *   runtime query, no allocation); a failure there returns GDN_ERR_HIP.
+ */
+#define GDN_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+gdn_status gdn_chunk_fwd_noalloc(const gdn_shape *s, const void *q, const void *k,
+                                 const void *v, const float *g, const float *beta,
+                                 const float *initial_state, const int32_t *cu_seqlens,
+                                 int32_t num_seqs, void *o, float *final_state,
+                                 hipStream_t stream);
+
+/*
  * gdn_recurrent_step: one decode token per sequence (the pages' "decode step's
  * recurrent" kernel).  s->T must be 1.
  *
