@@ -176,7 +176,7 @@ def bench_prefill(lib, b, synth, to_dev, steps, warmup):
     ms, kern = timed_chunk_calls(lib, calls, steps, warmup, 3)
     tokens = w.B * w.T
     flop, nbytes, cflop, cbytes = chunk_work(tokens, w.H_v)
-    names = ["plan", "prep", "carry"]
+    names = ["plan", "solve", "chain"]
     dom = max(range(3), key=lambda i: kern[i])
     return w, ms, dict(zip(names, kern)), names[dom], flop, nbytes, cflop, cbytes
 
@@ -213,9 +213,9 @@ def bench_next_rows(lib, b, synth, to_dev, dev, torch, np):
         out[f"prefill_t4096_h16_{H_v}"] = {
             "H_qk": 16, "H_v": H_v, "us_per_call": round(ms * 1e3, 2),
             "tokens_per_s": round(w.T / (ms / 1e3), 1),
-            "kernel_us": {k: round(v * 1e3, 2) for k, v in zip(["plan", "prep", "carry"], kern)},
+            "kernel_us": {k: round(v * 1e3, 2) for k, v in zip(["plan", "solve", "chain"], kern)},
             "roofline": roofline("mfma", cflop / (kern[2] / 1e3) / 1e12, MFMA_BF16_PEAK_TFLOPS, "TFLOP/s",
-                                 kernel="wy_chain_kernel")}
+                                 kernel="chain_kernel")}
         log(f"prefill 16/{H_v} heads: {ms * 1e3:.1f} us/call")
         del call
     # mixer steps at the prefill's shape (T = 4096, 16 qk / 32 v heads, d = 128)
@@ -339,14 +339,14 @@ def main():
                                                                   args.warmup)
     tokens = w.B * w.T
     value = tokens / (ms / 1e3)
-    kd = kern["carry"]
+    kd = kern["chain"]
     log(f"prefill: {ms * 1e3:.1f} us/step, kernels(us) " +
         ", ".join(f"{k}={v * 1e3:.1f}" for k, v in kern.items()))
-    # the chain kernel (state carry) dominates; its algorithmic work is its share of
-    # the method's FLOPs (the three state products W S, K^T U, Q' S), priced
+    # the chain kernel (state carry and output) dominates; its algorithmic work is its
+    # share of the method's FLOPs (the three state products K S, K^T U'', Q S), priced
     # against dense bf16 MFMA
     rl = roofline("mfma", cflop / (kd / 1e3) / 1e12, MFMA_BF16_PEAK_TFLOPS, "TFLOP/s",
-                  traffic=measured_traffic("wy_chain_kernel"), kernel="wy_chain_kernel",
+                  traffic=measured_traffic("chain_kernel"), kernel="chain_kernel",
                   kernel_us=round(kd * 1e3, 2), algorithmic_flop=cflop,
                   hbm_achieved=round(cbytes / (kd / 1e3) / 1e9, 1), hbm_peak=HBM_PEAK_GBS,
                   hbm_frac=round(cbytes / (kd / 1e3) / 1e9 / HBM_PEAK_GBS, 4))
@@ -423,9 +423,9 @@ def main():
         result["packed"] = {
             "workload": "packed_8seq", "tokens": wp.T, "us_per_call": round(msp * 1e3, 2),
             "tokens_per_s": round(wp.T / (msp / 1e3), 1),
-            "kernel_us": {k: round(v * 1e3, 2) for k, v in zip(["plan", "prep", "carry"], kp_)},
+            "kernel_us": {k: round(v * 1e3, 2) for k, v in zip(["plan", "solve", "chain"], kp_)},
             "roofline": roofline("mfma", cflop_p / (kp_[2] / 1e3) / 1e12, MFMA_BF16_PEAK_TFLOPS, "TFLOP/s",
-                                 kernel="wy_chain_kernel",
+                                 kernel="chain_kernel",
                                  mfma_frac=round(cflop_p / (kp_[2] / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)),
             "path_mfma_frac": round(flop_p / (msp / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
             "path_hbm_frac": round(bytes_p / (msp / 1e3) / 1e9 / HBM_PEAK_GBS, 4)}
@@ -442,7 +442,7 @@ def main():
         result["states"] = {
             "workload": "states_t2048", "tokens": ws_.T, "us_per_call": round(mss * 1e3, 2),
             "tokens_per_s": round(ws_.T / (mss / 1e3), 1),
-            "kernel_us": {k: round(v * 1e3, 2) for k, v in zip(["plan", "prep", "carry", "stream"], ks_)},
+            "kernel_us": {k: round(v * 1e3, 2) for k, v in zip(["plan", "solve", "chain", "stream"], ks_)},
             "roofline": roofline("hbm", sbytes / (ks_[3] / 1e3) / 1e9, HBM_PEAK_GBS, "GB/s",
                                  traffic=measured_traffic("stream_kernel"), kernel="stream_kernel",
                                  algorithmic_bytes=sbytes),
@@ -455,7 +455,7 @@ def main():
         result["states"]["strided_t_step_64"] = {
             "us_per_call": round(msx * 1e3, 2), "tokens_per_s": round(ws_.T / (msx / 1e3), 1),
             "states_kept": len(range(63, ws_.T, 64)),
-            "kernel_us": {k: round(v * 1e3, 2) for k, v in zip(["plan", "prep", "carry", "stream"], kx_)}}
+            "kernel_us": {k: round(v * 1e3, 2) for k, v in zip(["plan", "solve", "chain", "stream"], kx_)}}
         log(f"states, one per chunk: {msx * 1e3:.1f} us/call")
         del dsx, callx
 

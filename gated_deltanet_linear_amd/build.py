@@ -28,7 +28,8 @@ SAN_OUT = os.path.join(SAN_DIR, "libgdn_san.so")
 SAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
              "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-fno-sanitize-recover=undefined"]
 
-SOURCES = ["gdn_api.cpp", "gdn_step.hip", "gdn_chunk.hip", "gdn_wy.hip", "gdn_mixer.hip", "gdn_noalloc.hip"]
+SOURCES = ["gdn_api.cpp", "gdn_step.hip", "gdn_chunk.hip", "gdn_mixer.hip", "gdn_noalloc.hip",
+           "gdn_fused.hip"]
 
 # Packed-fp32 VALU forms are kept out of the generated code (the compiler would
 # otherwise form v_pk_{add,mul,fma}_f32 from ordinary float code).

@@ -1,7 +1,7 @@
 // The chunked paths of libgdn: the pieces every input type shares (the plan
 // kernel, the per-token states stream, the launchers and the workspace
-// layout) and the fp32 path (d_k = 16, chunk 16); bf16 inputs take the path in
-// gdn_wy.hip.
+// layout) and the general path (fp32 inputs at every supported size, bf16 at
+// chunk 32); bf16 inputs at chunk 64 take the fused path of gdn_fused.hip.
 //
 // What is computed is the gated delta rule of the pages (Qwen3.5 text
 // encyclopedia page, note "The DeltaNet mixer"; value table of
@@ -972,7 +972,7 @@ bool chunk_path_supported(const Problem &p) {
 
 // fp32 inputs at every supported (d_k, chunk), and bf16 inputs at chunk 32, take the
 // general path of this file (fp32: exact fp32 MFMA; bf16: hi/lo bf16 operands); bf16
-// at chunk 64 takes the W/U' path of gdn_wy.hip.
+// at chunk 64 takes the fused path of gdn_fused.hip.
 template <typename TIn, int DK>
 static hipError_t run_chunk(const Problem &p, const ChunkArgs &a, bool states, hipStream_t st) {
   if constexpr (std::is_same<TIn, float>::value) {
@@ -988,7 +988,7 @@ static hipError_t run_chunk(const Problem &p, const ChunkArgs &a, bool states, h
 hipError_t launch_chunk_path(const Problem &p, const ChunkArgs &a, bool states, hipStream_t st) {
   if (!chunk_path_supported(p)) return hipErrorInvalidValue;
   if (p.dtype == GDN_BF16) {
-    if (p.C == 64) return launch_wy_path(p, a, states, st);
+    if (p.C == 64) return launch_fused_path(p, a, states, st);
     return run_chunk<uint16_t, 128>(p, a, states, st);
   }
   return p.d_k == 16 ? run_chunk<float, 16>(p, a, states, st) : run_chunk<float, 128>(p, a, states, st);
@@ -1006,15 +1006,11 @@ Workspace workspace_layout(const Problem &p, bool states, void *base) {
   const size_t ss = take(sizeof(int32_t) * ((size_t)p.N + 1));
   const size_t cf = take(sizeof(int32_t) * ((size_t)p.N + 1));
   const size_t cc = (size_t)p.max_chunks * p.H_v;
-  const bool wy = p.dtype == GDN_BF16 && p.C == 64;  // the W/U' path of gdn_wy.hip
-  size_t tb = 0, pm = 0, eg = 0, eb = 0, wf = 0, qf = 0, uf = 0, of = 0, fc = 0, kt = 0;
-  if (wy) {
-    wf = take(kWyWBytes * cc);
-    qf = take(kWyQBytes * cc);
-    uf = take(sizeof(float) * cc * p.C * p.d_v);
-    of = take(sizeof(float) * cc * p.C * p.d_v);
-    fc = take(sizeof(float) * cc * kWyFac);
-    kt = take(kWyKtBytes * (size_t)p.max_chunks * p.H_qk);
+  const bool fused = p.dtype == GDN_BF16 && p.C == 64;  // the path of gdn_fused.hip
+  size_t tb = 0, pm = 0, eg = 0, eb = 0, tt = 0, kk = 0;
+  if (fused) {
+    tt = take(fused_t_bytes() * cc);
+    kk = take(fused_k_bytes() * (size_t)p.max_chunks * p.H_qk);
   } else {
     tb = take(sizeof(float) * cc * p.C * p.C);
     pm = take(sizeof(float) * cc * p.C * p.C);
@@ -1032,13 +1028,9 @@ Workspace workspace_layout(const Problem &p, bool states, void *base) {
     w.status = reinterpret_cast<int32_t *>(b + st);
     w.seq_start = reinterpret_cast<int32_t *>(b + ss);
     w.chunk_first = reinterpret_cast<int32_t *>(b + cf);
-    if (wy) {
-      w.wf = reinterpret_cast<unsigned char *>(b + wf);
-      w.qf = reinterpret_cast<unsigned char *>(b + qf);
-      w.uf = reinterpret_cast<float *>(b + uf);
-      w.of = reinterpret_cast<float *>(b + of);
-      w.fac = reinterpret_cast<float *>(b + fc);
-      w.ktf = reinterpret_cast<unsigned char *>(b + kt);
+    if (fused) {
+      w.tt = reinterpret_cast<unsigned char *>(b + tt);
+      w.kk = reinterpret_cast<unsigned char *>(b + kk);
     } else {
       w.tb = reinterpret_cast<float *>(b + tb);
       w.pm = reinterpret_cast<float *>(b + pm);

@@ -31,15 +31,11 @@ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 //   pm          f32 [max_chunks, H_v, C, C]   scale * (decay mask o Q K^T)
 //   eg          f32 [max_chunks, H_v, C]      exp(G_r)          (G: in-chunk cumsum of g)
 //   eb          f32 [max_chunks, H_v, C]      exp(G_last - G_r)
-//   (the fp32 path keeps tb, pm, eg, eb; the bf16 path keeps instead, per
-//    (chunk, value head) slot, the operands of its state carry in MFMA
-//    fragment order -- see gdn_wy.hip)
-//   wf          f16  [H_v, max_chunks, 16 KiB]   W = T diag(beta e^G) K^
-//   qf          f16  [H_v, max_chunks, 16 KiB]   Q' = diag(e^G) Q^ - P W
-//   uf          f32  [H_v, max_chunks, C, d_v]   U' = T diag(beta) V
-//   of          f32  [H_v, max_chunks, C, d_v]   O' = P U'
-//   fac         f32  [H_v, max_chunks, 80]       e^{G_last - G}, e^{G_last}
-//   ktf         f16  [H_qk, max_chunks, 16 KiB]  K^^T (normalised keys)
+//   (the general path keeps tb, pm, eg, eb; the fused bf16 path keeps instead,
+//    in MFMA fragment order -- see gdn_fused.hip)
+//   tt          [H_v, max_chunks, fused_t_bytes()]   T diag(beta) (fp16 hi/lo) and
+//                                                    the chain's per-token factors
+//   kk          [H_qk, max_chunks, fused_k_bytes()]  K and Q (fp16)
 //   (states path only)
 //   u           f32 [T_tot, H_v, d_v]        per-token write vectors
 //   sc          f32 [max_chunks, H_v, d_k, d_v]  state at each chunk start
@@ -48,15 +44,11 @@ struct Workspace {
   int32_t *seq_start = nullptr;
   int32_t *chunk_first = nullptr;
   float *tb = nullptr, *pm = nullptr, *eg = nullptr, *eb = nullptr;
-  unsigned char *wf = nullptr, *qf = nullptr, *ktf = nullptr;
-  float *uf = nullptr, *of = nullptr, *fac = nullptr;
+  unsigned char *tt = nullptr;  // fused bf16 path: T diag(beta) fragments and factors per (value head, chunk)
+  unsigned char *kk = nullptr;  // fused bf16 path: key and query fragments per (query/key head, chunk)
   float *u = nullptr, *sc = nullptr;
   size_t bytes = 0;
 };
-
-// Per-slot sizes of the bf16 path's carry operands (d_k = 128, C = 64).
-constexpr size_t kWyWBytes = 16384, kWyQBytes = 16384, kWyKtBytes = 16384;
-constexpr int kWyFac = 80;
 
 // Size of the static device scratch that gdn_chunk_fwd_noalloc uses as its workspace
 // (gdn_noalloc.hip), and its device address on the current device (looked up once
@@ -95,8 +87,11 @@ hipError_t launch_states_stream(const Problem &p, const ChunkArgs &a, const Seqs
 inline void mark_event(const ChunkArgs &a, int i, hipStream_t st) {
   if (a.events && i < a.n_events) (void)hipEventRecord(a.events[i], st);
 }
-// The bf16 chunked path (gdn_wy.hip): d_k = 128, C = 64.
-hipError_t launch_wy_path(const Problem &p, const ChunkArgs &a, bool states, hipStream_t stream);
+// The fused bf16 chunked path (gdn_fused.hip): d_k = 128, C = 64; bytes of its
+// per-(value head, chunk) workspace slot.
+hipError_t launch_fused_path(const Problem &p, const ChunkArgs &a, bool states, hipStream_t stream);
+size_t fused_t_bytes();
+size_t fused_k_bytes();
 
 // True when a chunked-path kernel is built for this problem.
 bool chunk_path_supported(const Problem &p);

@@ -82,7 +82,7 @@ def test_workspace_query_matches_layout():
     w = lib.gdn_chunk_fwd_workspace(ctypes.byref(s), 0)
     ws = lib.gdn_states_fwd_workspace(ctypes.byref(s), 0)
     chunks = 4096 // 64
-    per = 2 * 64 * 64 * 4 + 2 * 64 * 4                                  # T diag(beta), P, eg, eb
+    per = 2 * 6 * 64 * 16 + 8 * 64 * 4  # T diag(beta) fragments (fp16 hi and lo) and per-token factors
     assert w >= chunks * 32 * per
     assert ws >= w + 4096 * 32 * 128 * 4 + chunks * 32 * 128 * 128 * 4
 
