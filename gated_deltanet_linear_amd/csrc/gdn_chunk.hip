@@ -44,27 +44,48 @@ namespace gdn {
 constexpr float kGFloor = -1.0e4f;
 
 // ---------------------------------------------------------------------------
-// plan: sequence starts and the first global chunk of every sequence.
+// plan: sequence starts, the first global chunk of every sequence, and the
+// sequences ordered by length.
 // ---------------------------------------------------------------------------
 __global__ void plan_kernel(const int32_t *__restrict__ cu, int N, int T, int T_tot, int C,
                             int max_chunks, int32_t *__restrict__ status,
-                            int32_t *__restrict__ seq_start, int32_t *__restrict__ chunk_first) {
-  if (threadIdx.x != 0) return;
-  int bad = 0, acc = 0, prev = 0;
-  for (int n = 0; n <= N; ++n) {
-    const int s = cu ? cu[n] : n * T;
-    if ((n == 0 && s != 0) || s < prev || s > T_tot) bad = 1;
-    seq_start[n] = s;
-    chunk_first[n] = acc;
-    if (n < N) {
-      const int e = cu ? cu[n + 1] : (n + 1) * T;
-      if (e >= s) acc += (e - s + C - 1) / C;
+                            int32_t *__restrict__ seq_start, int32_t *__restrict__ chunk_first,
+                            int32_t *__restrict__ order) {
+  __shared__ int bad_s;
+  if (threadIdx.x == 0) {
+    int bad = 0, acc = 0, prev = 0;
+    for (int n = 0; n <= N; ++n) {
+      const int s = cu ? cu[n] : n * T;
+      if ((n == 0 && s != 0) || s < prev || s > T_tot) bad = 1;
+      seq_start[n] = s;
+      chunk_first[n] = acc;
+      if (n < N) {
+        const int e = cu ? cu[n + 1] : (n + 1) * T;
+        if (e >= s) acc += (e - s + C - 1) / C;
+      }
+      prev = s;
     }
-    prev = s;
+    if (N >= 0 && (cu ? cu[N] : N * T) != T_tot) bad = 1;
+    if (acc > max_chunks) bad = 1;
+    *status = bad;
+    bad_s = bad;
   }
-  if (N >= 0 && (cu ? cu[N] : N * T) != T_tot) bad = 1;
-  if (acc > max_chunks) bad = 1;
-  *status = bad;
+  __syncthreads();
+  // The sequences by decreasing chunk count (ties by index), so that the longest
+  // chains start first; past kOrderMaxSeqs sequences, their own order.
+  if (!order || bad_s) return;
+  for (int n = threadIdx.x; n < N; n += blockDim.x) {
+    int rank = n;
+    if (N <= kOrderMaxSeqs) {
+      const int ln = chunk_first[n + 1] - chunk_first[n];
+      rank = 0;
+      for (int m = 0; m < N; ++m) {
+        const int lm = chunk_first[m + 1] - chunk_first[m];
+        rank += lm > ln || (lm == ln && m < n);
+      }
+    }
+    order[rank] = n;
+  }
 }
 
 // Operand storage of a policy: bf16 path -> uint16_t (computed values as hi/lo
@@ -874,8 +895,8 @@ __global__ __launch_bounds__(256) void stream_kernel(
 // ---------------------------------------------------------------------------
 hipError_t launch_plan(const Problem &p, const ChunkArgs &a, hipStream_t st) {
   const Workspace &w = a.ws;
-  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(64), 0, st, a.cu, p.N, p.T, p.T_tot, p.C, p.max_chunks,
-                     w.status, w.seq_start, w.chunk_first);
+  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(256), 0, st, a.cu, p.N, p.T, p.T_tot, p.C, p.max_chunks,
+                     w.status, w.seq_start, w.chunk_first, w.order);
   return hipGetLastError();
 }
 
@@ -1005,6 +1026,7 @@ Workspace workspace_layout(const Problem &p, bool states, void *base) {
   const size_t st = take(sizeof(int32_t));
   const size_t ss = take(sizeof(int32_t) * ((size_t)p.N + 1));
   const size_t cf = take(sizeof(int32_t) * ((size_t)p.N + 1));
+  const size_t od = take(sizeof(int32_t) * ((size_t)p.N + 1));
   const size_t cc = (size_t)p.max_chunks * p.H_v;
   const bool fused = p.dtype == GDN_BF16 && p.C == 64;  // the path of gdn_fused.hip
   size_t tb = 0, pm = 0, eg = 0, eb = 0, tt = 0, kk = 0;
@@ -1028,6 +1050,7 @@ Workspace workspace_layout(const Problem &p, bool states, void *base) {
     w.status = reinterpret_cast<int32_t *>(b + st);
     w.seq_start = reinterpret_cast<int32_t *>(b + ss);
     w.chunk_first = reinterpret_cast<int32_t *>(b + cf);
+    w.order = reinterpret_cast<int32_t *>(b + od);
     if (fused) {
       w.tt = reinterpret_cast<unsigned char *>(b + tt);
       w.kk = reinterpret_cast<unsigned char *>(b + kk);

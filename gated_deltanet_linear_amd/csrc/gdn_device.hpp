@@ -151,12 +151,16 @@ __device__ __forceinline__ int find_seq(const int32_t *chunk_first, int N, int c
 
 // Where sequences and their chunks start.  Dense rows (no cu_seqlens, T > 0):
 // row n starts at token n T and its chunks at n ceil(T / C), no tables needed;
-// packed rows: the tables and the status word the plan kernel wrote.
+// packed rows: the tables and the status word the plan kernel wrote, and
+// optionally its order of the sequences by decreasing chunk count.
 struct Seqs {
   const int32_t *status, *seq_start, *chunk_first;
   int N;    // sequences
   int T;    // > 0: dense rows of T tokens; 0: use the tables
   int cpr;  // chunks per dense row
+  const int32_t *order = nullptr;  // packed rows: sequence of rank i by length (or null)
+  // the i-th sequence by decreasing length (dense rows: all alike, the i-th)
+  __device__ __forceinline__ int by_length(int i) const { return (T || !order) ? i : order[i]; }
   __device__ __forceinline__ bool bad() const { return T == 0 && *status != 0; }
   __device__ __forceinline__ int chunks() const { return T ? N * cpr : chunk_first[N]; }
   __device__ __forceinline__ int seq_of(int c) const { return T ? c / cpr : find_seq(chunk_first, N, c); }

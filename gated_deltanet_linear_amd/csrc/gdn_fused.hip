@@ -446,7 +446,8 @@ __global__ __launch_bounds__(64 * (NB + 3)) void chain_kernel(
   const int NCB = d_v / (16 * NB);
   const int u = xcd_group_remap(blockIdx.x, NCB * (H_v / H_qk), groups);
   if (u < 0) return;
-  const int jb = u % NCB, h = (u / NCB) % H_v, n = u / (NCB * H_v);
+  // packed sequences are taken longest first (the plan's order)
+  const int jb = u % NCB, h = (u / NCB) % H_v, n = sq.by_length(u / (NCB * H_v));
   const int j = h / (H_v / H_qk);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -491,6 +492,25 @@ __global__ __launch_bounds__(64 * (NB + 3)) void chain_kernel(
           for (int i = 0; i < 4; ++i)
             scw[(((int64_t)c * H_v + h) * DK + 16 * mt + 4 * lg + i) * d_v + cc] = S[mt][i];
       }
+      // K's fragments for K S, then the K^T fragments of K^T U'' (below), read now so
+      // that their latency passes under K S and T~ X.  Fragment (mt, st): lane (g, r) holds K[32 st + 4g + i][16 mt
+      // + r] and K[32 st + 16 + 4g + i][16 mt + r], i < 4: two transposed reads of the K
+      // fragments, where lane (g, 4e + q) of its group addresses token 32 st (+16) + 4g
+      // + e at d_k 16 mt + 4q, i.e. K fragment 4(2 st (+1)) + mt/2, lane 4g + e + 16q,
+      // half mt%2.
+      u32x4 kfr[16];
+#pragma unroll
+      for (int f = 0; f < 16; ++f) kfr[f] = P.kf[f][pl];
+      u32x4 ktf[8][2];
+#pragma unroll
+      for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+          const unsigned char *b = reinterpret_cast<const unsigned char *>(&P.kf[8 * st + (mt >> 1)][tslot]) + 8 * (mt & 1);
+          const u32x2 lo = lds_read_tr16(b), hi = lds_read_tr16(b + 4 * 64 * 16);
+          ktf[mt][st] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+        }
+      __builtin_amdgcn_sched_barrier(0);
       // K S: token tile m, four d_k steps
       f32x4 ks[4];
 #pragma unroll
@@ -498,7 +518,7 @@ __global__ __launch_bounds__(64 * (NB + 3)) void chain_kernel(
 #pragma unroll
       for (int s = 0; s < 4; ++s)
 #pragma unroll
-        for (int m = 0; m < 4; ++m) ks[m] = mfma_h(P.kf[4 * m + s][pl], sb[s], ks[m]);
+        for (int m = 0; m < 4; ++m) ks[m] = mfma_h(kfr[4 * m + s], sb[s], ks[m]);
       // X = V - diag(e^G rk) K S
       f32x4 x[4];
 #pragma unroll
@@ -549,20 +569,11 @@ __global__ __launch_bounds__(64 * (NB + 3)) void chain_kernel(
       u32x4 uh0, ul0, uh1, ul1;
       split8h(u2[0], u2[1], uh0, ul0);
       split8h(u2[2], u2[3], uh1, ul1);
-      // S <- e^{G_last} S + K^T U'' (the decayed state seeds the accumulator).  The K^T
-      // fragment (mt, st): lane (g, r) holds K[32 st + 4g + i][16 mt + r] and K[32 st + 16
-      // + 4g + i][16 mt + r], i < 4: two transposed reads of the K fragments, where the
-      // lane (g, 4e + q) of the group addresses token 32 st (+16) + 4g + e at d_k 16 mt
-      // + 4q: K fragment 4(2 st (+1)) + mt/2, lane 4g + e + 16q, half mt%2.
+      // S <- e^{G_last} S + K^T U'' (the decayed state seeds the accumulator)
       const float el = P.fac[FAC_EL][0];
-      auto ktf = [&](int mt, int st) {
-        const unsigned char *b = reinterpret_cast<const unsigned char *>(&P.kf[8 * st + (mt >> 1)][tslot]) + 8 * (mt & 1);
-        const u32x2 lo = lds_read_tr16(b), hi = lds_read_tr16(b + 4 * 64 * 16);
-        return u32x4{lo[0], lo[1], hi[0], hi[1]};
-      };
 #pragma unroll
       for (int mt = 0; mt < 8; ++mt) {
-        const u32x4 k0 = ktf(mt, 0), k1 = ktf(mt, 1);
+        const u32x4 k0 = ktf[mt][0], k1 = ktf[mt][1];
         f32x4 a = S[mt] * el;
         a = mfma_h(k0, uh0, a);
         a = mfma_h(k0, ul0, a);
@@ -781,6 +792,18 @@ hipError_t launch_chain(const Problem &p, const ChunkArgs &a, const Seqs &sq, hi
   return hipGetLastError();
 }
 
+// Compute units of the current device (looked up once per device).
+int cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  if (dev < 64 && cached[dev] > 0) return cached[dev];
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+  if (dev < 64) cached[dev] = n;
+  return n;
+}
+
 template <bool STATES, bool OBF16>
 hipError_t run_fused(const Problem &p, const ChunkArgs &a, hipStream_t st) {
   const Workspace &w = a.ws;
@@ -789,7 +812,7 @@ hipError_t run_fused(const Problem &p, const ChunkArgs &a, hipStream_t st) {
   const bool dense = dense_rows(p);
   if (!dense && (e = launch_plan(p, a, st)) != hipSuccess) return e;
   mark_event(a, 1, st);
-  const Seqs sq{w.status, w.seq_start, w.chunk_first, p.N, dense ? p.T : 0, dense ? ceil_div(p.T, C) : 0};
+  const Seqs sq{w.status, w.seq_start, w.chunk_first, p.N, dense ? p.T : 0, dense ? ceil_div(p.T, C) : 0, w.order};
   if (p.max_chunks > 0 && p.H_qk > 0) {
     hipLaunchKernelGGL(solve_kernel, dim3(p.max_chunks * p.H_qk), dim3(256), 0, st,
                        static_cast<const uint16_t *>(a.q), static_cast<const uint16_t *>(a.k), a.g, a.beta, sq,
@@ -797,7 +820,13 @@ hipError_t run_fused(const Problem &p, const ChunkArgs &a, hipStream_t st) {
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   mark_event(a, 2, st);
-  e = launch_chain<1, STATES, OBF16>(p, a, sq, st);
+  // Two column tiles per workgroup (their carries share the stage and P) once the
+  // single-tile grid would fill every CU twice over; one below that.
+  const long blocks1 = (long)p.N * p.H_v * (p.d_v / 16);
+  if (p.d_v % 32 == 0 && blocks1 >= 2L * cu_count())
+    e = launch_chain<2, STATES, OBF16>(p, a, sq, st);
+  else
+    e = launch_chain<1, STATES, OBF16>(p, a, sq, st);
   if (e != hipSuccess) return e;
   mark_event(a, 3, st);
   if constexpr (STATES) {

@@ -21,12 +21,15 @@ struct Problem {
 };
 
 inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
+// The plan kernel orders at most this many sequences by length (O(N^2) ranks).
+constexpr int kOrderMaxSeqs = 4096;
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 // Workspace of the chunked paths, carved out of the caller's buffer:
 //   status      int32            plan result: 0 ok, nonzero = bad cu_seqlens
 //   seq_start   int32 [N+1]      token offset of each sequence (cu_seqlens or n*T)
 //   chunk_first int32 [N+1]      global index of each sequence's first chunk
+//   order       int32 [N+1]      sequences by decreasing chunk count (plan kernel)
 //   tb          f32 [max_chunks, H_v, C, C]   T diag(beta), T = (I + A)^-1
 //   pm          f32 [max_chunks, H_v, C, C]   scale * (decay mask o Q K^T)
 //   eg          f32 [max_chunks, H_v, C]      exp(G_r)          (G: in-chunk cumsum of g)
@@ -43,6 +46,7 @@ struct Workspace {
   int32_t *status = nullptr;
   int32_t *seq_start = nullptr;
   int32_t *chunk_first = nullptr;
+  int32_t *order = nullptr;
   float *tb = nullptr, *pm = nullptr, *eg = nullptr, *eb = nullptr;
   unsigned char *tt = nullptr;  // fused bf16 path: T diag(beta) fragments and factors per (value head, chunk)
   unsigned char *kk = nullptr;  // fused bf16 path: key and query fragments per (query/key head, chunk)
