@@ -49,6 +49,34 @@ def parse():
     return ap.parse_args()
 
 
+def cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo), or None."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def rocm_version():
+    """The ROCm release of /opt/rocm and torch's HIP version."""
+    ver = None
+    try:
+        with open("/opt/rocm/.info/version") as f:
+            ver = f.read().strip()
+    except OSError:
+        pass
+    try:
+        import torch
+        hip = torch.version.hip
+    except Exception:
+        hip = None
+    return {"rocm": ver, "torch_hip": hip}
+
+
 def measured_traffic(kernel):
     """HBM bytes per launch of `kernel` from profiles/traffic.json, or None when absent
     or when the kernel's source file no longer matches the hash recorded with it."""
@@ -207,8 +235,8 @@ def bench_next_rows(lib, b, synth, to_dev, dev, torch, np):
     base = synth.WORKLOADS["prefill_t4096"]
     for H_v in (16, 48):
         w = dataclasses.replace(base, H_v=H_v)
-        call = prepare_chunk(lib, b, to_dev(synth.make_inputs(w, seed=0)))
-        ms, kern = timed_chunk_calls(lib, [call], 10, 3, 3)
+        calls = [prepare_chunk(lib, b, to_dev(synth.make_inputs(w, seed=s))) for s in range(N_SETS)]
+        ms, kern = timed_chunk_calls(lib, calls, 12, 3, 3)
         flop, nbytes, cflop, cbytes = chunk_work(w.T, H_v)
         out[f"prefill_t4096_h16_{H_v}"] = {
             "H_qk": 16, "H_v": H_v, "us_per_call": round(ms * 1e3, 2),
@@ -217,56 +245,67 @@ def bench_next_rows(lib, b, synth, to_dev, dev, torch, np):
             "roofline": roofline("mfma", cflop / (kern[2] / 1e3) / 1e12, MFMA_BF16_PEAK_TFLOPS, "TFLOP/s",
                                  kernel="chain_kernel")}
         log(f"prefill 16/{H_v} heads: {ms * 1e3:.1f} us/call")
-        del call
-    # mixer steps at the prefill's shape (T = 4096, 16 qk / 32 v heads, d = 128)
+        del calls
+    # mixer steps at the prefill's shape (T = 4096, 16 qk / 32 v heads, d = 128), each timed
+    # over N_SETS input and output sets in turn (more than the last-level cache holds)
     w = base
-    mi = synth.make_mixer_inputs(w, seed=0)
     bf = torch.bfloat16
-    x = torch.from_numpy(mi["x"]).to(dev, bf)
-    conv_w = torch.from_numpy(mi["conv_w"]).to(dev)
-    a = torch.from_numpy(mi["a"]).to(dev)
-    bb = torch.from_numpy(mi["b"]).to(dev)
-    A_log = torch.from_numpy(mi["A_log"]).to(dev)
-    dt_bias = torch.from_numpy(mi["dt_bias"]).to(dev)
-    z = torch.from_numpy(mi["z"]).to(dev, bf)
-    norm_w = torch.from_numpy(mi["norm_w"]).to(dev)
-    T, C = w.T, x.shape[2]
-    q = torch.empty((1, T, w.H_qk, w.d_k), dtype=bf, device=dev)
-    k = torch.empty_like(q)
-    v = torch.empty((1, T, w.H_v, w.d_v), dtype=bf, device=dev)
-    g = torch.empty((1, T, w.H_v), dtype=torch.float32, device=dev)
-    beta = torch.empty_like(g)
+    T = w.T
+    psets, nsets = [], []
+    for si in range(N_SETS):
+        mi = synth.make_mixer_inputs(w, seed=si)
+        x = torch.from_numpy(mi["x"]).to(dev, bf)
+        C = x.shape[2]
+        ps = dict(x=x, conv_w=torch.from_numpy(mi["conv_w"]).to(dev), a=torch.from_numpy(mi["a"]).to(dev),
+                  b=torch.from_numpy(mi["b"]).to(dev), A_log=torch.from_numpy(mi["A_log"]).to(dev),
+                  dt_bias=torch.from_numpy(mi["dt_bias"]).to(dev),
+                  q=torch.empty((1, T, w.H_qk, w.d_k), dtype=bf, device=dev),
+                  k=torch.empty((1, T, w.H_qk, w.d_k), dtype=bf, device=dev),
+                  v=torch.empty((1, T, w.H_v, w.d_v), dtype=bf, device=dev),
+                  g=torch.empty((1, T, w.H_v), dtype=torch.float32, device=dev),
+                  beta=torch.empty((1, T, w.H_v), dtype=torch.float32, device=dev))
+        ps["args"] = [P(ps["x"]), P(ps["conv_w"]), P(None), P(None), P(ps["a"]), P(ps["b"]), P(ps["A_log"]),
+                      P(ps["dt_bias"]), P(None), 0, P(ps["q"]), P(ps["k"]), P(ps["v"]), P(ps["g"]),
+                      P(ps["beta"]), stream]
+        psets.append(ps)
+        y = torch.from_numpy(np.random.default_rng(1 + si).standard_normal((1, T, w.H_v, w.d_v),
+                                                                             dtype=np.float32)).to(dev)
+        ns = dict(y=y, z=torch.from_numpy(mi["z"]).to(dev, bf), norm_w=torch.from_numpy(mi["norm_w"]).to(dev),
+                  yo=torch.empty_like(y))
+        ns["args"] = [P(ns["y"]), P(ns["z"]), P(ns["norm_w"]), ctypes.c_float(1e-6), P(ns["yo"]), stream]
+        nsets.append(ns)
     sp = b.GdnShape(1, T, w.H_qk, w.H_v, w.d_k, w.d_v, 1, 1.0, b.GDN_BF16, b.GDN_F32, 0)
-    pargs = [P(x), P(conv_w), P(None), P(None), P(a), P(bb), P(A_log), P(dt_bias), P(None), 0,
-             P(q), P(k), P(v), P(g), P(beta), stream]
+    turn = [0]
 
     def prologue():
-        if lib.gdn_mixer_prologue(ctypes.byref(sp), *pargs) != 0:
+        ps = psets[turn[0] % N_SETS]
+        turn[0] += 1
+        if lib.gdn_mixer_prologue(ctypes.byref(sp), *ps["args"]) != 0:
             raise RuntimeError(lib.gdn_last_error().decode())
-    ms = timed_launches(prologue, 50, 5, torch)
+    ms = timed_launches(prologue, 51, 6, torch)
     pbytes = T * C * 2 + C * 4 * 4 + 2 * T * w.H_v * 4 + T * C * 2 + 2 * T * w.H_v * 4
-    out["prologue_t4096"] = {"us_per_call": round(ms * 1e3, 2),
+    out["prologue_t4096"] = {"us_per_call": round(ms * 1e3, 2), "input_sets_rotated": N_SETS,
                              "roofline": roofline("hbm", pbytes / (ms / 1e3) / 1e9, HBM_PEAK_GBS, "GB/s",
                                                   traffic=measured_traffic("conv_silu_kernel"),
                                                   kernel="conv_silu_kernel (gates in the same launch)",
                                                   algorithmic_bytes=pbytes)}
     log(f"prologue: {ms * 1e3:.1f} us/call")
-    y = torch.from_numpy(np.random.default_rng(1).standard_normal((1, T, w.H_v, w.d_v), dtype=np.float32)).to(dev)
-    yo = torch.empty_like(y)
     sn = b.GdnShape(1, T, 1, w.H_v, 1, w.d_v, 1, 1.0, b.GDN_BF16, b.GDN_F32, 0)
-    nargs = [P(y), P(z), P(norm_w), ctypes.c_float(1e-6), P(yo), stream]
 
     def norm():
-        if lib.gdn_gated_norm(ctypes.byref(sn), *nargs) != 0:
+        ns = nsets[turn[0] % N_SETS]
+        turn[0] += 1
+        if lib.gdn_gated_norm(ctypes.byref(sn), *ns["args"]) != 0:
             raise RuntimeError(lib.gdn_last_error().decode())
-    ms = timed_launches(norm, 50, 5, torch)
+    ms = timed_launches(norm, 51, 6, torch)
     nbytes = T * w.H_v * w.d_v * (4 + 2 + 4) + w.d_v * 4
-    out["gated_norm_t4096"] = {"us_per_call": round(ms * 1e3, 2),
+    out["gated_norm_t4096"] = {"us_per_call": round(ms * 1e3, 2), "input_sets_rotated": N_SETS,
                                "roofline": roofline("hbm", nbytes / (ms / 1e3) / 1e9, HBM_PEAK_GBS, "GB/s",
                                                     traffic=measured_traffic("gated_norm_kernel"),
                                                     kernel="gated_norm_kernel", algorithmic_bytes=nbytes)}
     log(f"gated norm: {ms * 1e3:.1f} us/call")
-    del x, conv_w, a, bb, z, q, k, v, g, beta, y, yo
+    norm_w = nsets[0]["norm_w"]
+    del psets, nsets
     # the decode step with the output norm fused (256 sequences, as the decode row)
     wd = synth.WORKLOADS["decode_b256"]
     pool = synth.make_decode_pool(wd, seed=0)
@@ -367,6 +406,7 @@ def main():
                    "input_sets_rotated": N_SETS},
         "roofline": rl,
         "path": path,
+        "software": rocm_version(),
     }
 
     if not args.headline_only:
@@ -476,11 +516,25 @@ def main():
             if time.perf_counter() - t0 >= 10.0 or reps >= 400:
                 break
         dt = (time.perf_counter() - t0) / reps
+        # the same oracle on one core: 8 of the 32 heads, at least 5 s, scaled to all heads
+        heads1 = list(range(8))
+        t0 = time.perf_counter()
+        reps1 = 0
+        while True:
+            gdn_ref.recurrent(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], heads=heads1,
+                              want_final=False, nthreads=1)
+            reps1 += 1
+            if time.perf_counter() - t0 >= 5.0 or reps1 >= 100:
+                break
+        dt1 = (time.perf_counter() - t0) / reps1 * (w.H_v / len(heads1))
         result["cpu_baseline"] = {"value": round(tokens / dt, 1), "unit": "tokens/s", "cores": nthr,
-                                  "kind": "oracle",
+                                  "kind": "oracle", "cpu_model": cpu_model(),
+                                  "value_1core": round(tokens / dt1, 1),
                                   "sample": f"prefill_t4096, all 32 value heads x 4096 tokens, "
-                                            f"fp64 recurrence, {reps} repetition(s) of {dt:.2f} s"}
-        log(f"cpu oracle: {dt:.2f} s per prefill on {nthr} threads")
+                                            f"fp64 recurrence, {reps} repetition(s) of {dt:.2f} s on "
+                                            f"{nthr} threads; one core: heads 0-7, {reps1} repetition(s), "
+                                            f"scaled to 32 heads ({dt1:.2f} s per prefill)"}
+        log(f"cpu oracle: {dt:.2f} s per prefill on {nthr} threads, {dt1:.2f} s on one core")
     print(json.dumps(result), flush=True)
 
 

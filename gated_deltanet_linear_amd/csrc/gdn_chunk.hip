@@ -985,8 +985,7 @@ bool chunk_path_supported(const Problem &p) {
   if (p.d_v > 128) return false;
   if (p.dtype == GDN_BF16) {
     if (p.d_k != 128) return false;  // bf16 MFMA contracts over 32: d_k and C multiples of 32
-    if (p.C == 64) return p.d_v % 32 == 0;
-    return p.C == 32 && p.d_v % 16 == 0;
+    return (p.C == 64 || p.C == 32) && p.d_v % 16 == 0;
   }
   return (p.d_k == 16 || p.d_k == 128) && (p.C == 16 || p.C == 32 || p.C == 64) && p.d_v % 16 == 0;
 }

@@ -33,7 +33,9 @@ __device__ __forceinline__ void store4(uint16_t *p, const f32x4 &x) {
   *reinterpret_cast<u32x2 *>(p) = u32x2{(uint32_t)f2bf(x[0]) | ((uint32_t)f2bf(x[1]) << 16),
                                         (uint32_t)f2bf(x[2]) | ((uint32_t)f2bf(x[3]) << 16)};
 }
-__device__ __forceinline__ float silu(float x) { return x / (1.0f + __expf(-x)); }
+// x sigmoid(x) with the hardware reciprocal (1 ulp): a division's exact rounding
+// buys nothing for values that are then stored as bf16 or compared at 1e-5.
+__device__ __forceinline__ float silu(float x) { return x * __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
 
 // ---------------------------------------------------------------------------
 // Gated RMS norm: one row = one (token, value head), DV values; DV/4 lanes per

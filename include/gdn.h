@@ -83,12 +83,25 @@ typedef struct {
 
 /*
  * Built kernel set (anything else returns GDN_ERR_UNSUPPORTED):
- *   chunked paths:  dtype GDN_BF16 with d_k = 128, chunk = 64, d_v in {32, 64, 96, 128};
- *                   dtype GDN_BF16 with d_k = 128, chunk = 32, d_v in {16, 32, ..., 128};
+ *   chunked paths:  dtype GDN_BF16 with d_k = 128, chunk in {32, 64}, d_v in {16, 32, ..., 128};
  *                   dtype GDN_F32  with d_k in {16, 128}, chunk in {16, 32, 64},
  *                                  d_v in {16, 32, ..., 128}.
  *                   (bf16 MFMA contracts over 32 elements: bf16 needs d_k = 128.)
  *   decode step:    d_k in {16, 128}, d_v in {16, 128}, either dtype.
+ *
+ * Range of the bf16 path at chunk 64 (gdn_chunk_fwd, gdn_chunk_fwd_noalloc,
+ * gdn_states_fwd, gdn_states_fwd_strided): its matrix products take fp16
+ * operands.  q and k enter as fp16 (exact for bf16 values of magnitude in
+ * [6.1e-5, 65504]; smaller ones keep an absolute error below 3e-8, larger ones
+ * become infinities), and so do the state S and the per-chunk values derived
+ * from v (X = V - diag(e^G) K S, U = T diag(beta) X), each of which must stay
+ * below 65504 in magnitude: with |v| up to ~1e3 and decays and write strengths
+ * in their usual ranges they stay far inside.  A value past the range turns into
+ * an infinity or NaN that reaches o or the final state; the call then sets bit 1
+ * (value 2) of the int32 status word at the start of the workspace and its
+ * results are invalid.  Bit 0 (value 1) reports a malformed cu_seqlens array.
+ * The fp32 path, the bf16 path at chunk 32 and the decode step compute in fp32
+ * and have no such limit (their status word only ever holds bit 0).
  */
 
 /*

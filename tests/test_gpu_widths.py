@@ -102,3 +102,20 @@ def test_bf16_chunk32_all_heads():
     eo, ef, es = rel_max(host(o), ref["o"]), rel_fro(host(fin), ref["final"]), rel_fro(host(st), ref["states"])
     print(f"bf16 chunk 32: o {eo:.2e} final {ef:.2e} states {es:.2e}", flush=True)
     assert eo <= TOL_BF16_O and ef <= TOL_BF16_STATE and es <= TOL_BF16_STATE
+
+
+def test_bf16_chunk64_dv48_all_heads():
+    """Value width 48 (three 16-column tiles) on the bf16 chunk-64 path, packed, with states."""
+    gdn = _gdn()
+    w = dataclasses.replace(synth.WORKLOADS["prefill_t4096"], dtype="bf16", H_qk=2, H_v=4, d_v=48)
+    inp = synth.make_inputs(w, seed=14, lengths=(130, 1, 64, 77), s0_std=0.02)
+    d = to_dev(inp)
+    ref = gdn_ref.recurrent(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], s0=inp["s0"],
+                            cu_seqlens=inp["cu_seqlens"], want_states=True)
+    o, st, fin = gdn.gdn_states_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], initial_state=d["s0"],
+                                    cu_seqlens=d["cu"], chunk=64)
+    torch.cuda.synchronize()
+    eo, ef, es = rel_max(host(o), ref["o"]), rel_fro(host(fin), ref["final"]), rel_fro(host(st), ref["states"])
+    print(f"bf16 chunk 64, d_v 48: o {eo:.2e} final {ef:.2e} states {es:.2e}", flush=True)
+    assert eo <= TOL_BF16_O and ef <= TOL_BF16_STATE and es <= TOL_BF16_STATE
+    assert eo <= 2e-3
