@@ -396,6 +396,9 @@ def main():
             "mfma_TFLOPs": round(flop / (ms / 1e3) / 1e12, 2),
             "mfma_frac": round(flop / (ms / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
             "algorithmic_flop": flop, "algorithmic_bytes": nbytes}
+    ts, tc = measured_traffic("solve_kernel"), measured_traffic("chain_kernel")
+    path["traffic"] = None if ts is None or tc is None else ts + tc
+    path["traffic_over_algorithmic"] = None if path["traffic"] is None else round(path["traffic"] / nbytes, 3)
     result = {
         "metric": "GDN prefill tokens/s + decode steps/s on 1 MI355X; % MFMA/HBM roofline",
         "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
@@ -465,7 +468,7 @@ def main():
             "tokens_per_s": round(wp.T / (msp / 1e3), 1),
             "kernel_us": {k: round(v * 1e3, 2) for k, v in zip(["plan", "solve", "chain"], kp_)},
             "roofline": roofline("mfma", cflop_p / (kp_[2] / 1e3) / 1e12, MFMA_BF16_PEAK_TFLOPS, "TFLOP/s",
-                                 kernel="chain_kernel",
+                                 traffic=measured_traffic("chain_kernel_packed"), kernel="chain_kernel",
                                  mfma_frac=round(cflop_p / (kp_[2] / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)),
             "path_mfma_frac": round(flop_p / (msp / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
             "path_hbm_frac": round(bytes_p / (msp / 1e3) / 1e9 / HBM_PEAK_GBS, 4)}

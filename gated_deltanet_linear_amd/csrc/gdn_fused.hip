@@ -210,7 +210,11 @@ __global__ __launch_bounds__(256) void solve_kernel(const uint16_t *__restrict__
   if (blockIdx.x == 0 && threadIdx.x == 0 && seqs.T != 0) *status = 0;  // dense rows: no plan kernel clears it
   if (seqs.bad()) return;
   const int nch = seqs.chunks();
-  const int cpos = blockIdx.x / H_qk, j = blockIdx.x % H_qk;
+  // The query/key heads of one chunk share an XCD: they read the same rows of g and
+  // beta (a few bytes each per row), which that XCD's L2 then fetches once.
+  const int u = xcd_group_remap(blockIdx.x, H_qk, MC);
+  if (u < 0) return;
+  const int cpos = u / H_qk, j = u % H_qk;
   if (cpos >= nch) return;
   // Chunks run last to first: the chain's first chunks are the ones written last.
   const int c = nch - 1 - cpos;
@@ -814,7 +818,7 @@ hipError_t run_fused(const Problem &p, const ChunkArgs &a, hipStream_t st) {
   mark_event(a, 1, st);
   const Seqs sq{w.status, w.seq_start, w.chunk_first, p.N, dense ? p.T : 0, dense ? ceil_div(p.T, C) : 0, w.order};
   if (p.max_chunks > 0 && p.H_qk > 0) {
-    hipLaunchKernelGGL(solve_kernel, dim3(p.max_chunks * p.H_qk), dim3(256), 0, st,
+    hipLaunchKernelGGL(solve_kernel, dim3(xcd_group_grid(p.H_qk, p.max_chunks)), dim3(256), 0, st,
                        static_cast<const uint16_t *>(a.q), static_cast<const uint16_t *>(a.k), a.g, a.beta, sq,
                        w.status, w.tt, w.kk, p.H_qk, p.H_v, p.max_chunks, p.scale, p.l2norm ? 1 : 0);
     if ((e = hipGetLastError()) != hipSuccess) return e;
