@@ -105,9 +105,10 @@ class Prepared:
             raise RuntimeError(self.lib.gdn_last_error().decode())
 
 
-def prepare_chunk(lib, b, d, states=False, select=None):
+def prepare_chunk(lib, b, d, states=False, select=None, gated=None):
     """Bind a gdn_chunk_fwd (or gdn_states_fwd) call on device inputs d; with states and
-    select = (t_begin, t_end, t_step), a gdn_states_fwd_strided call."""
+    select = (t_begin, t_end, t_step), a gdn_states_fwd_strided call; with gated = (z,
+    weight), a gdn_chunk_fwd_gated call (eps 1e-6)."""
     import torch
     P = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())
     B, T, H_qk, d_k = d["q"].shape
@@ -137,10 +138,15 @@ def prepare_chunk(lib, b, d, states=False, select=None):
     else:
         need = lib.gdn_chunk_fwd_workspace(ctypes.byref(s), nseq)
         ws = torch.empty(need, dtype=torch.uint8, device=dev)
-        args = [P(d["q"]), P(d["k"]), P(d["v"]), P(d["g"]), P(d["beta"]), P(d["s0"]), P(d["cu"]), nseq,
-                P(o), P(fin), P(ws), need, stream]
-        keep = (o, fin, ws)
-        fn = lib.gdn_chunk_fwd
+        if gated is None:
+            args = [P(d["q"]), P(d["k"]), P(d["v"]), P(d["g"]), P(d["beta"]), P(d["s0"]), P(d["cu"]), nseq,
+                    P(o), P(fin), P(ws), need, stream]
+            fn = lib.gdn_chunk_fwd
+        else:
+            args = [P(d["q"]), P(d["k"]), P(d["v"]), P(d["g"]), P(d["beta"]), P(d["s0"]), P(d["cu"]), nseq,
+                    P(gated[0]), P(gated[1]), ctypes.c_float(1e-6), P(o), P(fin), P(ws), need, stream]
+            fn = lib.gdn_chunk_fwd_gated
+        keep = (o, fin, ws) + (gated or ())
     call = Prepared(lib, fn, s, args)
     call.keep = keep + (d,)   # the C call holds raw pointers: keep every tensor alive
     return call
@@ -473,7 +479,36 @@ def main():
             "path_mfma_frac": round(flop_p / (msp / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
             "path_hbm_frac": round(bytes_p / (msp / 1e3) / 1e9 / HBM_PEAK_GBS, 4)}
         log(f"packed: {msp * 1e3:.1f} us/call")
-        del dp, callp
+        # the same call with the mixer's output norm: fused into the chain (the head-wide
+        # chains run here: 8 sequences x 32 value heads), against the chunk call followed by
+        # the norm in place over its o
+        mi = synth.make_mixer_inputs(wp, seed=1)
+        zp = torch.from_numpy(mi["z"]).to(dev, torch.bfloat16)
+        nwp = torch.from_numpy(mi["norm_w"]).to(dev)
+        del mi
+        callg = prepare_chunk(lib, b, dp, gated=(zp, nwp))
+        msg, kg_ = timed_chunk_calls(lib, [callg], max(3, args.steps // 4), 2, 3)
+        op = callp.keep[0]
+        sn = b.GdnShape(1, wp.T, 1, wp.H_v, 1, wp.d_v, 1, 1.0, b.GDN_BF16, b.GDN_F32, 0)
+        nargs = [ctypes.c_void_p(op.data_ptr()), ctypes.c_void_p(zp.data_ptr()), ctypes.c_void_p(nwp.data_ptr()),
+                 ctypes.c_float(1e-6), ctypes.c_void_p(op.data_ptr()),
+                 ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)]
+
+        def chunk_then_norm():
+            callp()
+            if lib.gdn_gated_norm(ctypes.byref(sn), *nargs) != 0:
+                raise RuntimeError(lib.gdn_last_error().decode())
+        msn = timed_launches(chunk_then_norm, max(3, args.steps // 4), 2, torch)
+        el = wp.T * wp.H_v * wp.d_v
+        result["packed"]["gated"] = {
+            "us_per_call_fused": round(msg * 1e3, 2),
+            "kernel_us_fused": {k: round(v * 1e3, 2) for k, v in zip(["plan", "solve", "chain"], kg_)},
+            "us_per_call_chunk_then_norm": round(msn * 1e3, 2),
+            "o_bytes_not_moved": el * (4 + 4),
+            "note": "fused: the chain applies the norm and writes only the normed output (fp32); "
+                    "unfused: the chain writes o (fp32), the norm reads it back with z and rewrites it"}
+        log(f"packed with the output norm: fused {msg * 1e3:.1f} us/call, chunk then norm {msn * 1e3:.1f}")
+        del dp, callp, callg, zp, nwp
 
         # ---- states readout: T = 2048, 4 GiB of fp32 states --------------------------
         log("states_t2048: generating inputs and timing")

@@ -38,7 +38,8 @@ class GdnShape(ctypes.Structure):
                 ("o_dtype", ctypes.c_int32), ("flags", ctypes.c_uint32)]
 
 
-EXPORTS = ("gdn_chunk_fwd", "gdn_chunk_fwd_workspace", "gdn_chunk_fwd_noalloc", "gdn_recurrent_step", "gdn_states_fwd",
+EXPORTS = ("gdn_chunk_fwd", "gdn_chunk_fwd_workspace", "gdn_chunk_fwd_noalloc", "gdn_chunk_fwd_gated",
+           "gdn_recurrent_step", "gdn_states_fwd",
            "gdn_states_fwd_strided", "gdn_states_fwd_workspace", "gdn_gated_norm", "gdn_recurrent_step_gated",
            "gdn_mixer_prologue", "gdn_set_timing_events", "gdn_status_string",
            "gdn_last_error", "gdn_version")
@@ -74,6 +75,8 @@ def load_library(path: Optional[str] = None):
     F = ctypes.c_float
     lib.gdn_recurrent_step_gated.restype = ctypes.c_int
     lib.gdn_recurrent_step_gated.argtypes = [S, P, P, P, P, P, P, P, P, F, P, P]
+    lib.gdn_chunk_fwd_gated.restype = ctypes.c_int
+    lib.gdn_chunk_fwd_gated.argtypes = [S, P, P, P, P, P, P, P, I, P, P, F, P, P, P, Z, P]
     lib.gdn_gated_norm.restype = ctypes.c_int
     lib.gdn_gated_norm.argtypes = [S, P, P, P, F, P, P]
     lib.gdn_mixer_prologue.restype = ctypes.c_int
@@ -217,6 +220,39 @@ def gdn_chunk_fwd_noalloc(q, k, v, g, beta, initial_state=None, cu_seqlens=None,
                                    _stream(dev))
     _check(lib, st, "gdn_chunk_fwd_noalloc")
     return o, final_state
+
+
+def gdn_chunk_fwd_gated(q, k, v, g, beta, z, weight, eps=1e-6, initial_state=None, cu_seqlens=None,
+                        scale=None, chunk=None, l2norm=False, o_dtype=torch.float32,
+                        output_final_state=True, out=None, final_state=None, workspace=None):
+    """The chunked prompt path followed by the mixer's output norm: returns
+    (weight * o / sqrt(mean(o^2) + eps) * silu(z) per value head [B,T,H_v,d_v], final_state
+    or None); z is [B,T,H_v,d_v] in q's dtype, weight [d_v] fp32."""
+    lib = load_library()
+    dev, B, T, H_qk, H_v, d_k, d_v, N = _common(q, k, v, g, beta, initial_state, cu_seqlens)
+    _need(z, "z", (B, T, H_v, d_v), q.dtype, dev)
+    _need(weight, "weight", (d_v,), torch.float32, dev)
+    s = _shape(q, v, chunk, scale, l2norm, o_dtype, B, T)
+    if out is None:
+        out = torch.empty((B, T, H_v, d_v), dtype=o_dtype, device=dev)
+    _need(out, "out", (B, T, H_v, d_v), o_dtype, dev)
+    if output_final_state and final_state is None:
+        final_state = torch.empty((N, H_v, d_k, d_v), dtype=torch.float32, device=dev)
+    if final_state is not None:
+        _need(final_state, "final_state", (N, H_v, d_k, d_v), torch.float32, dev)
+    nseq = N if cu_seqlens is not None else 0
+    need = int(lib.gdn_chunk_fwd_workspace(ctypes.byref(s), nseq))
+    if need == 0:
+        _check(lib, lib.gdn_chunk_fwd_gated(ctypes.byref(s), *([None] * 7), nseq, None, None, float(eps),
+                                            None, None, None, 0, None), "gdn_chunk_fwd_gated")
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    st = lib.gdn_chunk_fwd_gated(ctypes.byref(s), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                 _ptr(initial_state), _ptr(cu_seqlens), nseq, _ptr(z), _ptr(weight),
+                                 float(eps), _ptr(out), _ptr(final_state), _ptr(workspace),
+                                 workspace.numel() * workspace.element_size(), _stream(dev))
+    _check(lib, st, "gdn_chunk_fwd_gated")
+    return out, final_state
 
 
 def gdn_states_fwd(q, k, v, g, beta, initial_state=None, cu_seqlens=None, scale=None, chunk=None,

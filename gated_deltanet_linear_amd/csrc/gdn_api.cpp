@@ -131,7 +131,8 @@ gdn_status chunked_common(const gdn_shape *s, const void *q, const void *k, cons
                           const float *beta, const float *initial_state, const int32_t *cu_seqlens,
                           int32_t num_seqs, void *o, float *states, float *final_state, void *workspace,
                           size_t workspace_bytes, hipStream_t stream, bool with_states, int32_t t_begin = 0,
-                          int32_t t_end = -1, int32_t t_step = 1) {
+                          int32_t t_end = -1, int32_t t_step = 1, const void *z = nullptr,
+                          const float *norm_w = nullptr, float eps = 0.0f, bool gated = false) {
   gdn::Problem p;
   gdn_status st = check_shape(s, cu_seqlens != nullptr, num_seqs, 0, p);
   if (st != GDN_OK) return st;
@@ -148,6 +149,11 @@ gdn_status chunked_common(const gdn_shape *s, const void *q, const void *k, cons
   if (any_tokens && (!q || !k || !v || !g || !beta)) return fail(GDN_ERR_NULL, "q, k, v, g and beta are required");
   if (!with_states && any_tokens && !o) return fail(GDN_ERR_NULL, "o is required");
   if (with_states && n_sel > 0 && p.B > 0 && !states) return fail(GDN_ERR_NULL, "states is required");
+  if (gated) {
+    if (!gdn::norm_supported(p)) return fail(GDN_ERR_UNSUPPORTED, "no output norm for d_v=%d", p.d_v);
+    if (!(eps >= 0.0f) || eps > 1e30f) return fail(GDN_ERR_SHAPE, "eps=%g", (double)eps);
+    if (any_tokens && (!z || !norm_w)) return fail(GDN_ERR_NULL, "z and weight are required");
+  }
   const gdn::Workspace need = gdn::workspace_layout(p, with_states, nullptr);
   if (!workspace) return fail(GDN_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need.bytes);
   if (workspace_bytes < need.bytes)
@@ -162,6 +168,10 @@ gdn_status chunked_common(const gdn_shape *s, const void *q, const void *k, cons
                       {states, "states", 16}, {final_state, "final_state", 4},
                       {workspace, "workspace", 16}};
   if ((st = check_alignment(args)) != GDN_OK) return st;
+  if (gated) {
+    const Arg gargs[] = {{z, "z", 4 * esize(p.dtype)}, {norm_w, "weight", 16}};
+    if ((st = check_alignment(gargs)) != GDN_OK) return st;
+  }
 
   const Tensors t = spans(p, q, k, v, g, beta, initial_state, cu_seqlens, o, states,
                           with_states ? (size_t)p.B * n_sel : 0, final_state, workspace, workspace_bytes);
@@ -182,6 +192,13 @@ gdn_status chunked_common(const gdn_shape *s, const void *q, const void *k, cons
   for (int a = 0; a < 4; ++a)
     for (int b = a + 1; b < 4; ++b)
       if (outs[a].s.overlaps(outs[b].s)) return fail(GDN_ERR_ALIAS, "%s overlaps %s", outs[a].name, outs[b].name);
+  if (gated) {
+    const Span sz(z, (size_t)p.T_tot * p.H_v * p.d_v * esize(p.dtype)), sw(norm_w, (size_t)p.d_v * sizeof(float));
+    for (const Out &x : outs) {
+      if (x.s.overlaps(sz)) return fail(GDN_ERR_ALIAS, "%s overlaps z", x.name);
+      if (x.s.overlaps(sw)) return fail(GDN_ERR_ALIAS, "%s overlaps weight", x.name);
+    }
+  }
 
   gdn::ChunkArgs a;
   a.q = q;
@@ -201,7 +218,19 @@ gdn_status chunked_common(const gdn_shape *s, const void *q, const void *k, cons
   a.ws = gdn::workspace_layout(p, with_states, workspace);
   a.events = g_events;
   a.n_events = g_n_events;
-  const hipError_t e = gdn::launch_chunk_path(p, a, with_states, stream);
+  // The output norm runs inside the chain where one workgroup holds a whole value head
+  // (the head-wide chains); elsewhere it follows the chain, in place over o.
+  const bool fused_norm = gated && !with_states && p.dtype == GDN_BF16 && gdn::fused_wide(p);
+  if (fused_norm) {
+    a.z = z;
+    a.nw = norm_w;
+    a.eps = eps;
+  }
+  hipError_t e = gdn::launch_chunk_path(p, a, with_states, stream);
+  if (e == hipSuccess && gated && !fused_norm && any_tokens) {
+    gdn::NormArgs na{o, z, norm_w, eps, o};
+    e = gdn::launch_gated_norm(p, na, stream);
+  }
   if (e != hipSuccess) return fail(GDN_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
   g_last_error.clear();
   return GDN_OK;
@@ -261,6 +290,20 @@ gdn_status gdn_chunk_fwd(const gdn_shape *s, const void *q, const void *k, const
   try {
     return chunked_common(s, q, k, v, g, beta, initial_state, cu_seqlens, num_seqs, o, nullptr, final_state,
                           workspace, workspace_bytes, stream, false);
+  } catch (const std::exception &e) {
+    return fail(GDN_ERR_HIP, "internal error: %s", e.what());
+  } catch (...) {
+    return fail(GDN_ERR_HIP, "internal error");
+  }
+}
+
+gdn_status gdn_chunk_fwd_gated(const gdn_shape *s, const void *q, const void *k, const void *v, const float *g,
+                               const float *beta, const float *initial_state, const int32_t *cu_seqlens,
+                               int32_t num_seqs, const void *z, const float *weight, float eps, void *out,
+                               float *final_state, void *workspace, size_t workspace_bytes, hipStream_t stream) {
+  try {
+    return chunked_common(s, q, k, v, g, beta, initial_state, cu_seqlens, num_seqs, out, nullptr, final_state,
+                          workspace, workspace_bytes, stream, false, 0, -1, 1, z, weight, eps, true);
   } catch (const std::exception &e) {
     return fail(GDN_ERR_HIP, "internal error: %s", e.what());
   } catch (...) {

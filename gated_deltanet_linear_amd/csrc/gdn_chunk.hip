@@ -1028,10 +1028,12 @@ Workspace workspace_layout(const Problem &p, bool states, void *base) {
   const size_t od = take(sizeof(int32_t) * ((size_t)p.N + 1));
   const size_t cc = (size_t)p.max_chunks * p.H_v;
   const bool fused = p.dtype == GDN_BF16 && p.C == 64;  // the path of gdn_fused.hip
-  size_t tb = 0, pm = 0, eg = 0, eb = 0, tt = 0, kk = 0;
+  size_t tb = 0, pm = 0, eg = 0, eb = 0, tt = 0, kk = 0, pf = 0;
+  const bool wide = fused && fused_wide(p);
   if (fused) {
     tt = take(fused_t_bytes() * cc);
     kk = take(fused_k_bytes() * (size_t)p.max_chunks * p.H_qk);
+    if (wide) pf = take(fused_p_bytes() * cc);
   } else {
     tb = take(sizeof(float) * cc * p.C * p.C);
     pm = take(sizeof(float) * cc * p.C * p.C);
@@ -1053,6 +1055,7 @@ Workspace workspace_layout(const Problem &p, bool states, void *base) {
     if (fused) {
       w.tt = reinterpret_cast<unsigned char *>(b + tt);
       w.kk = reinterpret_cast<unsigned char *>(b + kk);
+      if (wide) w.pf = reinterpret_cast<unsigned char *>(b + pf);
     } else {
       w.tb = reinterpret_cast<float *>(b + tb);
       w.pm = reinterpret_cast<float *>(b + pm);

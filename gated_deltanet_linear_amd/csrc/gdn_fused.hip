@@ -141,6 +141,18 @@ template <int N> __device__ __forceinline__ void wait_vm() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
+// Sum over the 16 lanes of each DPP row (lanes 16g .. 16g + 15), in every lane:
+// rotations by 8, 4, 2 and 1 within the row.
+__device__ __forceinline__ float row16_sum(float x) {
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x128, 0xf, 0xf, false));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x124, 0xf, 0xf, false));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x122, 0xf, 0xf, false));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x121, 0xf, 0xf, false));
+  return x;
+}
+__device__ __forceinline__ float silu_f(float x) { return x * __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
+constexpr int kSpinLimit = 1 << 20;  // bound of a wait between the waves of one workgroup (a hang guard)
+
 // The 6 lower fragments of a C x C lower-triangular A operand: (row tile m,
 // token step s) with 32 s <= 16 m + 15.
 __device__ __forceinline__ constexpr int tri_frag(int m, int s) { return m < 2 ? m : 2 * m - 2 + s; }
@@ -164,6 +176,8 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const void *p) {
 constexpr size_t kTFragBytes = 2 * kTriFrags * 64 * 16;
 enum { FAC_GL2 = 0, FAC_EKR, FAC_FKR, FAC_EQR, FAC_RK, FAC_RQ, FAC_EL, kFacRows = 8 };
 constexpr size_t kTBytes = kTFragBytes + kFacRows * C * 4;
+// Per (value head, chunk), head-wide chains only: P's hi/lo A fragments, as T~'s.
+constexpr size_t kPBytes = 2 * kTriFrags * 64 * 16;
 // Per (query/key head, chunk): 16 K fragments, then 16 Q fragments (fp16).
 constexpr size_t kKFragBytes = 16 * 64 * 16;
 constexpr size_t kKBytes = 2 * kKFragBytes;
@@ -201,11 +215,13 @@ __device__ __forceinline__ f32x4 block_mm_acc(const float *X, int ib, int m, con
   return acc;
 }
 
+template <bool WP>  // WP: also P's fragments, for head-wide chains
 __global__ __launch_bounds__(256) void solve_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
                                                     const float *__restrict__ g, const float *__restrict__ beta,
                                                     const Seqs seqs, int32_t *__restrict__ status,
                                                     unsigned char *__restrict__ tt, unsigned char *__restrict__ kk,
-                                                    int H_qk, int H_v, int MC, float scale, int l2norm) {
+                                                    unsigned char *__restrict__ pf, int H_qk, int H_v, int MC,
+                                                    float scale, int l2norm) {
   __shared__ SolveSmem sm;
   if (blockIdx.x == 0 && threadIdx.x == 0 && seqs.T != 0) *status = 0;  // dense rows: no plan kernel clears it
   if (seqs.bad()) return;
@@ -307,6 +323,23 @@ __global__ __launch_bounds__(256) void solve_kernel(const uint16_t *__restrict__
         a = mfma_bf16(*reinterpret_cast<const bf16x8 *>(Ab + k0), *reinterpret_cast<const bf16x8 *>(Bb + k0), a);
     }
     gt[qq] = a;
+  }
+  // For head-wide chains, K Q^T for P: wave w takes query tile m = w, key tiles ni <= m:
+  // D(ni, m) holds, in lane l, query 16m + l%16 at keys 16ni + 4g + i, the A operand of
+  // P U once the key tiles are paired (2s, 2s + 1).
+  f32x4 gp[4];
+#pragma unroll
+  for (int ni = 0; ni < 4; ++ni) gp[ni] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if constexpr (WP) {
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni) {
+      if (ni <= w) {
+        const uint16_t *Ab = sk + (ni * 16 + lr) * LDK + 8 * lg, *Bb = sq + (w * 16 + lr) * LDK + 8 * lg;
+#pragma unroll
+        for (int k0 = 0; k0 < DK; k0 += 32)
+          gp[ni] = mfma_bf16(*reinterpret_cast<const bf16x8 *>(Ab + k0), *reinterpret_cast<const bf16x8 *>(Bb + k0), gp[ni]);
+      }
+    }
   }
   __syncthreads();  // the key and query rows are dead: ra holds A and rt holds T from here
 
@@ -412,6 +445,33 @@ __global__ __launch_bounds__(256) void solve_kernel(const uint16_t *__restrict__
           }
           u32x4 hi, lo;
           split8h(a, b, hi, lo);
+          const int f = tri_frag(m, s);
+          dst[(2 * f) * 64 + lane] = hi;
+          dst[(2 * f + 1) * 64 + lane] = lo;
+        }
+      }
+    }
+    // P[r][i] = rq_r rk_i e^{G_r - G_i} (q_r . k_i), i <= r, as fp16 hi/lo A fragments
+    // (row tile m = w), for head-wide chains
+    if constexpr (WP) {
+      const int m = w, r = 16 * m + lr;
+      const double gr = sm.gam[r];
+      const float rq = sm.rq[r];
+      f32x4 d[4];
+#pragma unroll
+      for (int ni = 0; ni < 4; ++ni) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = 16 * ni + 4 * lg + e;
+          d[ni][e] = (ni <= m && i <= r) ? rq * sm.rk[i] * fexp((float)(gr - sm.gam[i])) * gp[ni][e] : 0.f;
+        }
+      }
+      u32x4 *dst = reinterpret_cast<u32x4 *>(pf + ((int64_t)h * MC + c) * kPBytes);
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        if (s <= (m >> 1)) {
+          u32x4 hi, lo;
+          split8h(d[2 * s], d[2 * s + 1], hi, lo);
           const int f = tri_frag(m, s);
           dst[(2 * f) * 64 + lane] = hi;
           dst[(2 * f + 1) * 64 + lane] = lo;
@@ -784,6 +844,419 @@ __global__ __launch_bounds__(64 * (NB + 3)) void chain_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// wide chain: one (sequence, value head) per workgroup of 5 waves, for workloads
+// whose sequences x value heads fill every CU (d_v = 128).  Waves 0-3 each own two
+// 16-column tiles of S and run, for chunk c, both the carry (K S, X, T~ X, K^T U'')
+// and those tiles' output diag(e^G rq) Q S + P U from their own S and U registers,
+// each operand read from LDS serving both tiles; wave 4 copies chunk c + 1's K, Q,
+// T~, P (formed by the solve for these chains), factors and v rows into the other
+// LDS stage.  One barrier per chunk.  A head's eight tiles then run on the CU's
+// four MFMA units at once, where the narrow chain runs one or two carries per CU.
+// ---------------------------------------------------------------------------
+constexpr int kWideCols = 8;                  // 16-column tiles of a head (d_v = 128)
+constexpr int kTPW = 1;                       // tiles per column wave
+constexpr int kWideWaves = kWideCols / kTPW;  // column waves
+struct WideStage {
+  u32x4 kf[16][64];             // K fragments, slot kf_slot(l) (copied)
+  u32x4 qf[16][64];             // Q fragments, slot kf_slot(l) (copied)
+  u32x4 tf[2 * kTriFrags][64];  // T~ hi/lo (copied)
+  u32x4 pf[2 * kTriFrags][64];  // P hi/lo: fragment 2 tri_frag(m, s) + (0 hi, 1 lo) (copied; formed by the solve)
+  u32x4 vr[16][64];             // v rows (bf16): row r's 16-byte chunk k in slot 16 r + (k ^ r % 16) (copied)
+  float fac[kFacRows][C];       // the per-token factors (copied)
+};
+struct WideSmem {
+  WideStage st[2];
+  float red[2][kWideCols][C];  // gated output: per-token sums of squares of each tile
+  int cnt[2];                  // gated output: waves that have written red[b], cumulative
+};
+
+// GATED: o is not stored; the output stage writes weight * o / sqrt(mean(o^2) + eps) *
+// silu(z) instead, the mean over the head's d_v values, which the tiles' waves add up
+// through LDS (a bounded wait: past kSpinLimit polls it sets status bit 2 and goes on).
+template <bool STATES, bool OBF16, bool GATED>
+__global__ __launch_bounds__(64 * (kWideWaves + 1)) void wide_kernel(
+    const uint16_t *__restrict__ v, const float *__restrict__ s0, const Seqs sq, const unsigned char *__restrict__ tt,
+    const unsigned char *__restrict__ kk, const unsigned char *__restrict__ pfw, int32_t *__restrict__ status,
+    void *__restrict__ o, float *__restrict__ fin, float *__restrict__ uw, float *__restrict__ scw, int H_qk,
+    int H_v, int MC, int groups, const uint16_t *__restrict__ zg, const float *__restrict__ nw, float eps) {
+  __shared__ WideSmem sm;
+  if (sq.bad()) return;
+  constexpr int d_v = 16 * kWideCols;
+  // (sequence, query/key head) groups of H_v / H_qk value heads, longest sequences first
+  const int u = xcd_group_remap(blockIdx.x, H_v / H_qk, groups);
+  if (u < 0) return;
+  const int h = u % H_v, n = sq.by_length(u / H_v);
+  const int j = h / (H_v / H_qk);
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lr = lane & 15, lg = lane >> 4;
+  const int fs = kf_slot(lane);
+  const int c_begin = sq.first(n), c_end = sq.first(n + 1);
+  const int s_begin = sq.start(n), s_end = sq.start(n + 1);
+  const int nit = c_end - c_begin;
+
+  if constexpr (GATED) {
+    if (threadIdx.x < 2) sm.cnt[threadIdx.x] = 0;  // before the first barrier
+  }
+  if (wave < kWideWaves) {
+    // ---------------------------- column waves -------------------------------
+    // Wave w owns the kTPW 16-column tiles jt = kTPW w + t; each operand read from LDS
+    // feeds all of them.
+    const int tslot = kf_slot(4 * (lane >> 4) + ((lane >> 2) & 3) + 16 * (lane & 3));  // transposed-read slot
+    const int64_t sbase = (int64_t)(n * H_v + h) * DK;
+    int cc[kTPW];
+#pragma unroll
+    for (int t = 0; t < kTPW; ++t) cc[t] = 16 * (kTPW * wave + t) + lr;
+    f32x4 S[kTPW][8];  // S[t][mt]: rows 16 mt + 4g + i, column cc[t]
+    u32x4 sb[kTPW][4];
+#pragma unroll
+    for (int t = 0; t < kTPW; ++t) {
+#pragma unroll
+      for (int mt = 0; mt < 8; ++mt) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) S[t][mt][i] = s0 ? s0[(sbase + 16 * mt + 4 * lg + i) * d_v + cc[t]] : 0.f;
+      }
+#pragma unroll
+      for (int s = 0; s < 4; ++s) sb[t][s] = h16x8(S[t][2 * s], S[t][2 * s + 1]);
+    }
+    // v in accumulator order by an identity MFMA on its bf16 rows (token 16m + l%16,
+    // columns 4g .. 4g + 3 in the first half of the step; B selects column l%16).
+    u32x4 vsel;
+    {
+      uint32_t wv[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (4 * lg + e == lr) wv[e >> 1] |= 0x3f80u << (16 * (e & 1));  // bf16 1.0
+      vsel = u32x4{wv[0], wv[1], wv[2], wv[3]};
+    }
+    constexpr int esz = OBF16 ? 2 : 4;
+    bool bad = false, late = false;
+    const float wcol = GATED ? nw[cc[0]] : 0.f;
+    auto step = [&](int it) {
+      const int c = c_begin + it;
+      const WideStage &P = sm.st[it & 1];
+      const int t0 = s_begin + it * C;
+      const int len = min(C, s_end - t0);
+      if constexpr (STATES) {
+        // the state at the chunk start
+#pragma unroll
+        for (int t = 0; t < kTPW; ++t)
+#pragma unroll
+          for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              scw[(((int64_t)c * H_v + h) * DK + 16 * mt + 4 * lg + i) * d_v + cc[t]] = S[t][mt][i];
+      }
+      // K S: token tile m, four d_k steps
+      f32x4 ks[kTPW][4];
+#pragma unroll
+      for (int t = 0; t < kTPW; ++t)
+#pragma unroll
+        for (int m = 0; m < 4; ++m) ks[t][m] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const u32x4 kfr = P.kf[4 * m + s][fs];
+#pragma unroll
+          for (int t = 0; t < kTPW; ++t) ks[t][m] = mfma_h(kfr, sb[t][s], ks[t][m]);
+        }
+      // X = V - diag(e^G rk) K S, V: row 16m + l%16, columns 16 jt + 4g .. + 3 (half g%2 of
+      // v row chunk 2 jt + g/2) moved to accumulator order
+      u32x4 xh[kTPW][2], xl[kTPW][2];
+#pragma unroll
+      for (int t = 0; t < kTPW; ++t) {
+        const int jt = kTPW * wave + t;
+        f32x4 x[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const int r = 16 * m + lr;
+          const u32x2 vr = *reinterpret_cast<const u32x2 *>(
+              reinterpret_cast<const unsigned char *>(&P.vr[0][0]) + (16 * r + ((2 * jt + (lg >> 1)) ^ lr)) * 16 +
+              8 * (lg & 1));
+          const f32x4 vv = mfma_bf16(__builtin_bit_cast(bf16x8, u32x4{vr[0], vr[1], 0u, 0u}),
+                                     __builtin_bit_cast(bf16x8, vsel), f32x4{0.f, 0.f, 0.f, 0.f});
+          const f32x4 e = *reinterpret_cast<const f32x4 *>(&P.fac[FAC_EKR][16 * m + 4 * lg]);
+          x[m] = vv - e * ks[t][m];
+        }
+        split8h(x[0], x[1], xh[t][0], xl[t][0]);
+        split8h(x[2], x[3], xh[t][1], xl[t][1]);
+      }
+      // U = T~ X (lower triangular: token tile m needs steps s <= m / 2)
+      f32x4 uacc[kTPW][4];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+#pragma unroll
+        for (int t = 0; t < kTPW; ++t) uacc[t][m] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          if (s == 0 || m >= 2) {
+            const int f = 2 * tri_frag(m, s);
+            const u32x4 th = P.tf[f][lane], tl = P.tf[f + 1][lane];
+#pragma unroll
+            for (int t = 0; t < kTPW; ++t) {
+              uacc[t][m] = mfma_h(th, xh[t][s], uacc[t][m]);
+              uacc[t][m] = mfma_h(th, xl[t][s], uacc[t][m]);
+              uacc[t][m] = mfma_h(tl, xh[t][s], uacc[t][m]);
+            }
+          }
+        }
+      }
+      if constexpr (STATES) {
+        // the tokens' write vectors, rows t0 .. t0 + len
+        const auto rs = rows_rsrc(uw + (int64_t)t0 * H_v * d_v, (int64_t)len * H_v * d_v * 4);
+#pragma unroll
+        for (int t = 0; t < kTPW; ++t)
+#pragma unroll
+          for (int m = 0; m < 4; ++m)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const float xv = uacc[t][m][i];
+              __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(xv), rs,
+                                                    (((16 * m + 4 * lg + i) * H_v + h) * d_v + cc[t]) * 4, 0, 0);
+            }
+      }
+      // The output first (its registers are free again for the state update):
+      // o = diag(e^G rq) Q S + P U for these tiles, stored rows t0 .. t0 + len.
+      if constexpr (GATED) {
+        static_assert(kTPW == 1, "the gated output is written for one tile per wave");
+        // the gate z of this tile: rows 16m + l%16, columns 16 jt + 4g .. + 3 (bf16)
+        u32x2 zr[4];
+        {
+          const auto rz = rows_rsrc(const_cast<uint16_t *>(zg) + (int64_t)t0 * H_v * d_v, (int64_t)len * H_v * d_v * 2);
+#pragma unroll
+          for (int m = 0; m < 4; ++m)
+            zr[m] = __builtin_bit_cast(
+                u32x2, __builtin_amdgcn_raw_buffer_load_b64(rz, (((16 * m + lr) * H_v + h) * d_v + cc[0] - lr + 4 * lg) * 2,
+                                                            0, 0));
+        }
+        u32x4 pu_h[2], pu_l[2];
+        split8h(uacc[0][0], uacc[0][1], pu_h[0], pu_l[0]);
+        split8h(uacc[0][2], uacc[0][3], pu_h[1], pu_l[1]);
+        f32x4 oa[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int s = 0; s < 4; ++s) acc = mfma_h(P.qf[4 * m + s][fs], sb[0][s], acc);
+          acc = acc * *reinterpret_cast<const f32x4 *>(&P.fac[FAC_EQR][16 * m + 4 * lg]);
+#pragma unroll
+          for (int s = 0; s < 2; ++s) {
+            if (s == 0 || m >= 2) {
+              const int f = 2 * tri_frag(m, s);
+              acc = mfma_h(P.pf[f][lane], pu_h[s], acc);
+              acc = mfma_h(P.pf[f][lane], pu_l[s], acc);
+              acc = mfma_h(P.pf[f + 1][lane], pu_h[s], acc);
+            }
+          }
+          oa[m] = acc;
+        }
+        // this tile's share of each token's sum of squares (row 16m + 4g + i), then the
+        // head's total from all tiles' shares
+        const int rb = it & 1;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          f32x4 ps;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) ps[i] = row16_sum(oa[m][i] * oa[m][i]);
+          if (lr == 0) *reinterpret_cast<f32x4 *>(&sm.red[rb][kTPW * wave][16 * m + 4 * lg]) = ps;
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+        if (lane == 0) __hip_atomic_fetch_add(&sm.cnt[rb], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        const int target = kWideWaves * ((it >> 1) + 1);
+        for (int spins = 0; __hip_atomic_load(&sm.cnt[rb], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < target;) {
+          if (++spins > kSpinLimit) {
+            late = true;
+            break;
+          }
+          __builtin_amdgcn_s_sleep(1);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+        const auto ro = rows_rsrc(o ? static_cast<unsigned char *>(o) + (int64_t)t0 * H_v * d_v * esz : nullptr,
+                                  o ? (int64_t)len * H_v * d_v * esz : 0);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          f32x4 tot = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int jj = 0; jj < kWideCols; ++jj) tot += *reinterpret_cast<const f32x4 *>(&sm.red[rb][jj][16 * m + 4 * lg]);
+          const f32x4 zz = mfma_bf16(__builtin_bit_cast(bf16x8, u32x4{zr[m][0], zr[m][1], 0u, 0u}),
+                                     __builtin_bit_cast(bf16x8, vsel), f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float rs = rsqrtf(tot[i] * (1.0f / d_v) + eps);
+            const float xv = wcol * (oa[m][i] * rs) * silu_f(zz[i]);
+            bad |= 16 * m + 4 * lg + i < len && !__builtin_isfinite(xv);
+            const int off = (((16 * m + 4 * lg + i) * H_v + h) * d_v + cc[0]) * esz;
+            if constexpr (OBF16)
+              __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(pk_bf16(xv, 0.f) & 0xffffu), ro, off, 0, 0);
+            else
+              __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(xv), ro, off, 0, 0);
+          }
+        }
+      } else {
+        u32x4 pu_h[kTPW][2], pu_l[kTPW][2];
+#pragma unroll
+        for (int t = 0; t < kTPW; ++t) {
+          split8h(uacc[t][0], uacc[t][1], pu_h[t][0], pu_l[t][0]);
+          split8h(uacc[t][2], uacc[t][3], pu_h[t][1], pu_l[t][1]);
+        }
+        const auto ro = rows_rsrc(o ? static_cast<unsigned char *>(o) + (int64_t)t0 * H_v * d_v * esz : nullptr,
+                                  o ? (int64_t)len * H_v * d_v * esz : 0);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          f32x4 acc[kTPW];
+#pragma unroll
+          for (int t = 0; t < kTPW; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int s = 0; s < 4; ++s) {
+            const u32x4 qf = P.qf[4 * m + s][fs];
+#pragma unroll
+            for (int t = 0; t < kTPW; ++t) acc[t] = mfma_h(qf, sb[t][s], acc[t]);
+          }
+          const f32x4 eq = *reinterpret_cast<const f32x4 *>(&P.fac[FAC_EQR][16 * m + 4 * lg]);
+#pragma unroll
+          for (int t = 0; t < kTPW; ++t) acc[t] = acc[t] * eq;
+#pragma unroll
+          for (int s = 0; s < 2; ++s) {
+            if (s == 0 || m >= 2) {
+              const int f = 2 * tri_frag(m, s);
+              const u32x4 ph = P.pf[f][lane], pl = P.pf[f + 1][lane];
+#pragma unroll
+              for (int t = 0; t < kTPW; ++t) {
+                acc[t] = mfma_h(ph, pu_h[t][s], acc[t]);
+                acc[t] = mfma_h(ph, pu_l[t][s], acc[t]);
+                acc[t] = mfma_h(pl, pu_h[t][s], acc[t]);
+              }
+            }
+          }
+#pragma unroll
+          for (int t = 0; t < kTPW; ++t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              bad |= 16 * m + 4 * lg + i < len && !__builtin_isfinite(acc[t][i]);
+              const int off = (((16 * m + 4 * lg + i) * H_v + h) * d_v + cc[t]) * esz;
+              const float xv = acc[t][i];
+              if constexpr (OBF16)
+                __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(pk_bf16(xv, 0.f) & 0xffffu), ro, off, 0, 0);
+              else
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(xv), ro, off, 0, 0);
+            }
+        }
+      }
+      // U'' = diag(e^{G_last - G} rk) U and S <- e^{G_last} S + K^T U''
+      u32x4 uh[kTPW][2], ul[kTPW][2];
+#pragma unroll
+      for (int t = 0; t < kTPW; ++t) {
+        f32x4 u2[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+          u2[m] = uacc[t][m] * *reinterpret_cast<const f32x4 *>(&P.fac[FAC_FKR][16 * m + 4 * lg]);
+        split8h(u2[0], u2[1], uh[t][0], ul[t][0]);
+        split8h(u2[2], u2[3], uh[t][1], ul[t][1]);
+      }
+      // The K^T fragment (mt, st) by two transposed reads of the K fragments: lane
+      // (g, 4e + q) of a group addresses token 32 st (+16) + 4g + e at d_k 16 mt + 4q,
+      // i.e. K fragment 4(2 st (+1)) + mt/2, lane 4g + e + 16q, half mt%2.
+      auto ktf = [&](int mt, int st) {
+        const unsigned char *b = reinterpret_cast<const unsigned char *>(&P.kf[8 * st + (mt >> 1)][tslot]) + 8 * (mt & 1);
+        const u32x2 lo = lds_read_tr16(b), hi = lds_read_tr16(b + 4 * 64 * 16);
+        return u32x4{lo[0], lo[1], hi[0], hi[1]};
+      };
+      const float el = P.fac[FAC_EL][0];
+#pragma unroll
+      for (int mt = 0; mt < 8; ++mt) {
+        const u32x4 k0 = ktf(mt, 0), k1 = ktf(mt, 1);
+#pragma unroll
+        for (int t = 0; t < kTPW; ++t) {
+          f32x4 a = S[t][mt] * el;
+          a = mfma_h(k0, uh[t][0], a);
+          a = mfma_h(k0, ul[t][0], a);
+          a = mfma_h(k1, uh[t][1], a);
+          S[t][mt] = mfma_h(k1, ul[t][1], a);
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < kTPW; ++t)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) sb[t][s] = h16x8(S[t][2 * s], S[t][2 * s + 1]);
+      lds_barrier();
+    };
+    lds_barrier();
+    for (int it = 0; it < nit; ++it) step(it);
+    if (fin) {
+#pragma unroll
+      for (int t = 0; t < kTPW; ++t)
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) fin[(sbase + 16 * mt + 4 * lg + i) * d_v + cc[t]] = S[t][mt][i];
+    }
+    // a non-finite stored o or final state flags the call (an fp16 overflow of a carried operand)
+#pragma unroll
+    for (int t = 0; t < kTPW; ++t)
+#pragma unroll
+      for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) bad |= !__builtin_isfinite(S[t][mt][i]);
+    if (__builtin_amdgcn_ballot_w64(bad) != 0 && lane == 0) atomicOr(status, 2);
+    if (__builtin_amdgcn_ballot_w64(late) != 0 && lane == 0) atomicOr(status, 4);
+  } else {
+    // ------------------------------ copy wave --------------------------------
+    // K, Q, T~, P fragments, the factors and the v rows of chunk c into stage b: global
+    // -> LDS loads, lane l's 16 bytes to the block's slot l.
+    auto prep = [&](int b, int c) {
+      WideStage &S = sm.st[b];
+      const u32x4 *ksrc = reinterpret_cast<const u32x4 *>(kk + ((int64_t)j * MC + c) * kKBytes) + lane;
+      const u32x4 *tsrc = reinterpret_cast<const u32x4 *>(tt + ((int64_t)h * MC + c) * kTBytes) + lane;
+      const u32x4 *psrc = reinterpret_cast<const u32x4 *>(pfw + ((int64_t)h * MC + c) * kPBytes) + lane;
+#pragma unroll
+      for (int f = 0; f < 16; ++f) lds_copy16(ksrc + f * 64, &S.kf[f][0]);
+#pragma unroll
+      for (int f = 0; f < 16; ++f) lds_copy16(ksrc + (16 + f) * 64, &S.qf[f][0]);
+#pragma unroll
+      for (int f = 0; f < 2 * kTriFrags; ++f) lds_copy16(tsrc + f * 64, &S.tf[f][0]);
+#pragma unroll
+      for (int f = 0; f < 2 * kTriFrags; ++f) lds_copy16(psrc + f * 64, &S.pf[f][0]);
+      lds_copy16(tsrc + 2 * kTriFrags * 64, &S.fac[0][0]);
+      lds_copy16(tsrc + (2 * kTriFrags + 1) * 64, &S.fac[4][0]);
+      // v rows: instruction f, lane l -> row 4f + l/16, slot l%16, which holds the row's
+      // chunk (l%16) ^ (row % 16); rows past the length repeat its last row (their
+      // products are zero: T~ has no entries there and the factors are zero)
+      {
+        const int t0 = s_begin + (c - c_begin) * C;
+        const int len = min(C, s_end - t0);
+#pragma unroll
+        for (int f = 0; f < 16; ++f) {
+          const int row = 4 * f + (lane >> 4), r = min(row, len - 1), k = (lane & 15) ^ (row & 15);
+          lds_copy16(reinterpret_cast<const unsigned char *>(v) + (((int64_t)(t0 + r) * H_v + h) * d_v + 8 * k) * 2,
+                     &S.vr[f][0]);
+        }
+      }
+      wait_vm<0>();
+    };
+    if (nit > 0) prep(0, c_begin);
+    lds_barrier();
+    for (int it = 0; it < nit; ++it) {
+      if (it + 1 < nit) prep((it + 1) & 1, c_begin + it + 1);
+      lds_barrier();
+    }
+  }
+}
+
+template <bool STATES, bool OBF16, bool GATED>
+hipError_t launch_wide(const Problem &p, const ChunkArgs &a, const Seqs &sq, hipStream_t st) {
+  const Workspace &w = a.ws;
+  const int groups = p.N * p.H_qk;
+  if (groups == 0) return hipSuccess;
+  const int grid = xcd_group_grid(p.H_v / p.H_qk, groups);
+  hipLaunchKernelGGL((wide_kernel<STATES, OBF16, GATED>), dim3(grid), dim3(64 * (kWideWaves + 1)), 0, st,
+                     static_cast<const uint16_t *>(a.v), a.s0, sq, w.tt, w.kk, w.pf, w.status, a.o, a.final_state,
+                     w.u, w.sc, p.H_qk, p.H_v, p.max_chunks, groups, static_cast<const uint16_t *>(a.z), a.nw,
+                     a.eps);
+  return hipGetLastError();
+}
+
 template <int NB, bool STATES, bool OBF16>
 hipError_t launch_chain(const Problem &p, const ChunkArgs &a, const Seqs &sq, hipStream_t st) {
   const Workspace &w = a.ws;
@@ -818,16 +1291,29 @@ hipError_t run_fused(const Problem &p, const ChunkArgs &a, hipStream_t st) {
   mark_event(a, 1, st);
   const Seqs sq{w.status, w.seq_start, w.chunk_first, p.N, dense ? p.T : 0, dense ? ceil_div(p.T, C) : 0, w.order};
   if (p.max_chunks > 0 && p.H_qk > 0) {
-    hipLaunchKernelGGL(solve_kernel, dim3(xcd_group_grid(p.H_qk, p.max_chunks)), dim3(256), 0, st,
-                       static_cast<const uint16_t *>(a.q), static_cast<const uint16_t *>(a.k), a.g, a.beta, sq,
-                       w.status, w.tt, w.kk, p.H_qk, p.H_v, p.max_chunks, p.scale, p.l2norm ? 1 : 0);
+    const dim3 sgrid(xcd_group_grid(p.H_qk, p.max_chunks));
+    if (w.pf)
+      hipLaunchKernelGGL(solve_kernel<true>, sgrid, dim3(256), 0, st, static_cast<const uint16_t *>(a.q),
+                         static_cast<const uint16_t *>(a.k), a.g, a.beta, sq, w.status, w.tt, w.kk, w.pf, p.H_qk,
+                         p.H_v, p.max_chunks, p.scale, p.l2norm ? 1 : 0);
+    else
+      hipLaunchKernelGGL(solve_kernel<false>, sgrid, dim3(256), 0, st, static_cast<const uint16_t *>(a.q),
+                         static_cast<const uint16_t *>(a.k), a.g, a.beta, sq, w.status, w.tt, w.kk, w.pf, p.H_qk,
+                         p.H_v, p.max_chunks, p.scale, p.l2norm ? 1 : 0);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   mark_event(a, 2, st);
-  // Two column tiles per workgroup (their carries share the stage and P) once the
-  // single-tile grid would fill every CU twice over; one below that.
+  // A whole value head per workgroup once sequences x value heads fill every CU;
+  // else two column tiles per workgroup (their carries share the stage and P) once
+  // the single-tile grid would fill every CU twice over; one below that.
   const long blocks1 = (long)p.N * p.H_v * (p.d_v / 16);
-  if (p.d_v % 32 == 0 && blocks1 >= 2L * cu_count())
+  if (fused_wide(p)) {
+    if (!STATES && a.z)
+      e = launch_wide<false, OBF16, true>(p, a, sq, st);
+    else
+      e = launch_wide<STATES, OBF16, false>(p, a, sq, st);
+  }
+  else if (p.d_v % 32 == 0 && blocks1 >= 2L * cu_count())
     e = launch_chain<2, STATES, OBF16>(p, a, sq, st);
   else
     e = launch_chain<1, STATES, OBF16>(p, a, sq, st);
@@ -843,6 +1329,11 @@ hipError_t run_fused(const Problem &p, const ChunkArgs &a, hipStream_t st) {
 }  // namespace
 
 size_t fused_t_bytes() { return kTBytes; }
+size_t fused_p_bytes() { return kPBytes; }
+bool fused_wide(const Problem &p) {
+  return p.dtype == GDN_BF16 && p.C == C && p.d_k == DK && p.d_v == 16 * kWideCols &&
+         (long)p.N * p.H_v >= cu_count();
+}
 size_t fused_k_bytes() { return kKBytes; }
 
 hipError_t launch_fused_path(const Problem &p, const ChunkArgs &a, bool states, hipStream_t st) {

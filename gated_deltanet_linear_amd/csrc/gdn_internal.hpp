@@ -39,6 +39,7 @@ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 //   tt          [H_v, max_chunks, fused_t_bytes()]   T diag(beta) (fp16 hi/lo) and
 //                                                    the chain's per-token factors
 //   kk          [H_qk, max_chunks, fused_k_bytes()]  K and Q (fp16)
+//   pf          [H_v, max_chunks, fused_p_bytes()]   P (fp16 hi/lo), head-wide chains only
 //   (states path only)
 //   u           f32 [T_tot, H_v, d_v]        per-token write vectors
 //   sc          f32 [max_chunks, H_v, d_k, d_v]  state at each chunk start
@@ -50,6 +51,7 @@ struct Workspace {
   float *tb = nullptr, *pm = nullptr, *eg = nullptr, *eb = nullptr;
   unsigned char *tt = nullptr;  // fused bf16 path: T diag(beta) fragments and factors per (value head, chunk)
   unsigned char *kk = nullptr;  // fused bf16 path: key and query fragments per (query/key head, chunk)
+  unsigned char *pf = nullptr;  // fused bf16 path, head-wide chains: P fragments per (value head, chunk)
   float *u = nullptr, *sc = nullptr;
   size_t bytes = 0;
 };
@@ -78,6 +80,10 @@ struct ChunkArgs {
   Workspace ws;
   hipEvent_t *events = nullptr;  // optional timing hook: recorded around each launch
   int n_events = 0;
+  // gated output (chunk path only, where fused_wide(): o <- nw * o / sqrt(mean(o^2) + eps) * silu(z))
+  const void *z = nullptr;
+  const float *nw = nullptr;
+  float eps = 0.0f;
 };
 hipError_t launch_chunk_path(const Problem &p, const ChunkArgs &a, bool states, hipStream_t stream);
 
@@ -96,6 +102,9 @@ inline void mark_event(const ChunkArgs &a, int i, hipStream_t st) {
 hipError_t launch_fused_path(const Problem &p, const ChunkArgs &a, bool states, hipStream_t stream);
 size_t fused_t_bytes();
 size_t fused_k_bytes();
+size_t fused_p_bytes();
+// True when the fused path runs one workgroup per (sequence, value head) for this problem.
+bool fused_wide(const Problem &p);
 
 // True when a chunked-path kernel is built for this problem.
 bool chunk_path_supported(const Problem &p);

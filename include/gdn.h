@@ -136,8 +136,40 @@ gdn_status gdn_chunk_fwd(const gdn_shape *s, const void *q, const void *k,
                          hipStream_t stream);
 
 /* Workspace bytes gdn_chunk_fwd needs for this shape; num_seqs is N when the
-   call will pass cu_seqlens, else 0.  Returns 0 if the shape is invalid. */
+   call will pass cu_seqlens, else 0.  Returns 0 if the shape is invalid.  It is
+   also what gdn_chunk_fwd_gated needs. */
 size_t gdn_chunk_fwd_workspace(const gdn_shape *s, int32_t num_seqs);
+
+/*
+ * gdn_chunk_fwd_gated: gdn_chunk_fwd followed by the mixer's output norm, the
+ * norm(y, gate = silu(z)) with gain `weight` that the mixer applies to the rule's
+ * output (Qwen3.5 text encyclopedia page, note "The DeltaNet mixer"): per token and
+ * value head, over that head's d_v values,
+ *     out = weight * o / sqrt(mean(o^2) + eps) * silu(z).
+ *   Arguments as gdn_chunk_fwd's, with o replaced by
+ *   z              [B, T, H_v, d_v]   dtype (the gate input)
+ *   weight         [d_v] float32, 16-byte aligned
+ *   eps            >= 0
+ *   out            [B, T, H_v, d_v]   o_dtype (written); must not overlap any input
+ *   d_v must be one of 16, 32, 64, 128, 256 (the norm's widths).
+ * Where the chain runs one workgroup per (sequence, value head) -- bf16 inputs at
+ * chunk 64 with d_v = 128 once sequences x value heads reach the GPU's compute-unit
+ * count -- the norm is applied in the chain's output stage and o itself is never
+ * written; elsewhere the chain writes o into `out` and the norm then runs in place
+ * over it (one more pass over out and z; with a bf16 out, o is then rounded to bf16
+ * before the norm reads it, so the result carries two roundings instead of one).  In the fused case the waves of a
+ * workgroup exchange their shares of each token's sum of squares through LDS with a
+ * bounded wait; a wait that exceeds its bound sets bit 2 (value 4) of the status word
+ * at the start of the workspace (the results are then invalid).  Status bits 0 and 1
+ * as for gdn_chunk_fwd.
+ */
+gdn_status gdn_chunk_fwd_gated(const gdn_shape *s, const void *q, const void *k,
+                               const void *v, const float *g, const float *beta,
+                               const float *initial_state, const int32_t *cu_seqlens,
+                               int32_t num_seqs, const void *z, const float *weight,
+                               float eps, void *out, float *final_state,
+                               void *workspace, size_t workspace_bytes,
+                               hipStream_t stream);
 
 /*
  * gdn_chunk_fwd_noalloc: gdn_chunk_fwd for callers that cannot allocate device

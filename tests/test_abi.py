@@ -107,3 +107,27 @@ def test_strided_states_selection_is_validated():
     # 3 selected tokens of 32 heads x 128 x 128 fp32 = 6 MiB of states: placed to end inside v
     states = ctypes.c_void_p(v.value - 2 * 1024 * 1024)
     assert call(0, 128, 50, states=states) == 5
+
+
+def test_gated_chunk_call_is_validated():
+    """gdn_chunk_fwd_gated: the norm's widths, eps >= 0, z and weight present, aligned and
+    disjoint from every output."""
+    lib = _lib()
+    q, k, v, g, b, o, fin, ws, z, w = _ptrs(10)
+
+    def call(s, z=z, w=w, eps=1e-6, out=o):
+        need = lib.gdn_chunk_fwd_workspace(ctypes.byref(s), 0)
+        return lib.gdn_chunk_fwd_gated(ctypes.byref(s), q, k, v, g, b, None, None, 0, z, w, eps, out, fin,
+                                       ws, need, None)
+    s = _shape()
+    assert call(_shape(d_v=48)) == 4                                   # no norm of width 48
+    assert call(s, eps=-1.0) == 2
+    assert call(s, eps=float("nan")) == 2
+    assert call(s, z=None) == 1
+    assert call(s, w=None) == 1
+    assert call(s, z=ctypes.c_void_p(z.value + 2)) == 6                # z: 4 elements
+    assert call(s, w=ctypes.c_void_p(w.value + 4)) == 6                # weight: 16 bytes
+    assert call(s, out=ctypes.c_void_p(z.value + 256)) == 5            # out overlaps z
+    assert b"overlaps z" in lib.gdn_last_error()
+    assert call(s, w=ctypes.c_void_p(fin.value + 64)) == 5             # final_state overlaps weight
+    assert b"overlaps weight" in lib.gdn_last_error()

@@ -1,9 +1,10 @@
 """GPU parity of the bf16 prompt path when each chain workgroup carries two column tiles
 of the state (taken once the one-tile grid holds at least two workgroups per compute unit:
-here 16 query/key and 32 value heads of width 128, with two or more sequences), and of the
-longest-first order of packed sequences.  o and the final state of every head, and the
-per-token states of sampled heads, against the oracle at the bf16 tolerances (2e-2 x RMS on
-o, 1e-3 relative on states).
+here 16 query/key and 32 value heads of width 128, with two or more sequences) or a whole
+value head (taken once sequences x value heads reach the compute-unit count, 256 on an
+MI355X: here nine sequences), and of the longest-first order of packed sequences.  o and
+the final state of every head, and the per-token states of sampled heads, against the
+oracle at the bf16 tolerances (2e-2 x RMS on o, 1e-3 relative on states).
 """
 import numpy as np
 import pytest
@@ -60,4 +61,11 @@ def test_packed_longest_first_two_tiles():
     lens = (65, 200, 1, 130, 0, 77)
     print(f"packed lengths {lens}, 16/32 heads, initial states", flush=True)
     inp = synth.make_inputs(synth.WORKLOADS["packed_8seq"], seed=22, lengths=lens, s0_std=0.02)
+    _check(inp, states=True)
+
+
+def test_packed_whole_head_workgroups():
+    lens = (65, 1, 130, 0, 77, 64, 200, 33, 5)
+    print(f"packed lengths {lens}: {len(lens)} x 32 value heads, initial states", flush=True)
+    inp = synth.make_inputs(synth.WORKLOADS["packed_8seq"], seed=23, lengths=lens, s0_std=0.02)
     _check(inp, states=True)
