@@ -474,7 +474,8 @@ def main():
             "tokens_per_s": round(wp.T / (msp / 1e3), 1),
             "kernel_us": {k: round(v * 1e3, 2) for k, v in zip(["plan", "solve", "chain"], kp_)},
             "roofline": roofline("mfma", cflop_p / (kp_[2] / 1e3) / 1e12, MFMA_BF16_PEAK_TFLOPS, "TFLOP/s",
-                                 traffic=measured_traffic("chain_kernel_packed"), kernel="chain_kernel",
+                                 traffic=measured_traffic("wide_kernel_packed"),
+                                 kernel="wide_kernel (one workgroup per sequence and value head)",
                                  mfma_frac=round(cflop_p / (kp_[2] / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)),
             "path_mfma_frac": round(flop_p / (msp / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
             "path_hbm_frac": round(bytes_p / (msp / 1e3) / 1e9 / HBM_PEAK_GBS, 4)}
@@ -505,6 +506,8 @@ def main():
             "kernel_us_fused": {k: round(v * 1e3, 2) for k, v in zip(["plan", "solve", "chain"], kg_)},
             "us_per_call_chunk_then_norm": round(msn * 1e3, 2),
             "o_bytes_not_moved": el * (4 + 4),
+            "chain_traffic_fused": measured_traffic("wide_kernel_gated"),
+            "chain_traffic_unfused": measured_traffic("wide_kernel_packed"),
             "note": "fused: the chain applies the norm and writes only the normed output (fp32); "
                     "unfused: the chain writes o (fp32), the norm reads it back with z and rewrites it"}
         log(f"packed with the output norm: fused {msg * 1e3:.1f} us/call, chunk then norm {msn * 1e3:.1f}")

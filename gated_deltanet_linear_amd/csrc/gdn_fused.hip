@@ -151,7 +151,19 @@ __device__ __forceinline__ float row16_sum(float x) {
   return x;
 }
 __device__ __forceinline__ float silu_f(float x) { return x * __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
-constexpr int kSpinLimit = 1 << 20;  // bound of a wait between the waves of one workgroup (a hang guard)
+// The value x of lane `src` (0 .. 63), through the LDS crossbar (no memory access).
+__device__ __forceinline__ float lane_read(float x, int src) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(4 * src, __builtin_bit_cast(int, x)));
+}
+// Four consecutive output values at byte offset off of a row range: 16 bytes (fp32) or
+// 8 bytes (bf16, rounded to nearest even).
+template <bool OBF16>
+__device__ __forceinline__ void store_o4(__amdgpu_buffer_rsrc_t r, int off, const f32x4 &x) {
+  if constexpr (OBF16)
+    __builtin_amdgcn_raw_buffer_store_b64(u32x2{pk_bf16(x[0], x[1]), pk_bf16(x[2], x[3])}, r, off, 0, 0);
+  else
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), r, off, 0, 0);
+}
 
 // The 6 lower fragments of a C x C lower-triangular A operand: (row tile m,
 // token step s) with 32 s <= 16 m + 15.
@@ -867,13 +879,13 @@ struct WideStage {
 };
 struct WideSmem {
   WideStage st[2];
-  float red[2][kWideCols][C];  // gated output: per-token sums of squares of each tile
-  int cnt[2];                  // gated output: waves that have written red[b], cumulative
+  float red[2][C][kWideCols];  // gated output: each tile's share of each token's sum of squares
 };
 
-// GATED: o is not stored; the output stage writes weight * o / sqrt(mean(o^2) + eps) *
-// silu(z) instead, the mean over the head's d_v values, which the tiles' waves add up
-// through LDS (a bounded wait: past kSpinLimit polls it sets status bit 2 and goes on).
+// GATED: o is not stored; the kernel writes weight * o / sqrt(mean(o^2) + eps) * silu(z)
+// instead, the mean over the head's d_v values.  The tiles' waves leave their shares of
+// each chunk's sums of squares in LDS and finish the chunk's output after the barrier
+// that closes its step, so the sums need no wait of their own.
 template <bool STATES, bool OBF16, bool GATED>
 __global__ __launch_bounds__(64 * (kWideWaves + 1)) void wide_kernel(
     const uint16_t *__restrict__ v, const float *__restrict__ s0, const Seqs sq, const unsigned char *__restrict__ tt,
@@ -896,9 +908,6 @@ __global__ __launch_bounds__(64 * (kWideWaves + 1)) void wide_kernel(
   const int s_begin = sq.start(n), s_end = sq.start(n + 1);
   const int nit = c_end - c_begin;
 
-  if constexpr (GATED) {
-    if (threadIdx.x < 2) sm.cnt[threadIdx.x] = 0;  // before the first barrier
-  }
   if (wave < kWideWaves) {
     // ---------------------------- column waves -------------------------------
     // Wave w owns the kTPW 16-column tiles jt = kTPW w + t; each operand read from LDS
@@ -931,8 +940,41 @@ __global__ __launch_bounds__(64 * (kWideWaves + 1)) void wide_kernel(
       vsel = u32x4{wv[0], wv[1], wv[2], wv[3]};
     }
     constexpr int esz = OBF16 ? 2 : 4;
-    bool bad = false, late = false;
-    const float wcol = GATED ? nw[cc[0]] : 0.f;
+    bool bad = false;
+    // gated output: this lane's 4 columns of the tile, their gains, and the o and z of
+    // the chunk whose output waits for the barrier that closed its step
+    const int c0 = 16 * kTPW * wave + 4 * lg;
+    f32x4 wg = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (GATED) wg = *reinterpret_cast<const f32x4 *>(nw + c0);
+    f32x4 ok[4] = {};
+    u32x2 zk[4] = {};
+    // Chunk it's normed output.  It runs inside step it + 1, between U = T~ X and that
+    // chunk's output stage (which overwrites ok and zk), without a branch around it so
+    // that its arithmetic can interleave with the step's MFMAs; `live` false (no chunk
+    // before the first) stores nothing: the row range is empty.
+    auto finish = [&](int it, bool live) {
+      const int t0 = s_begin + it * C;
+      const int len = live ? min(C, s_end - t0) : 0;
+      // token 16g + l%16 = lane: its sum of squares over the head, then 1 / RMS
+      const f32x4 ra = *reinterpret_cast<const f32x4 *>(&sm.red[it & 1][lane][0]);
+      const f32x4 rb = *reinterpret_cast<const f32x4 *>(&sm.red[it & 1][lane][4]);
+      const float tot = ((ra[0] + ra[1]) + (ra[2] + ra[3])) + ((rb[0] + rb[1]) + (rb[2] + rb[3]));
+      const float inv = rsqrtf(tot * (1.0f / d_v) + eps);
+      const auto ro = rows_rsrc(o && live ? static_cast<unsigned char *>(o) + (int64_t)t0 * H_v * d_v * esz : nullptr,
+                                o ? (int64_t)len * H_v * d_v * esz : 0);
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const float r = lane_read(inv, 16 * m + lr);  // token 16m + l%16
+        const f32x4 zf = {__uint_as_float(zk[m][0] << 16), __uint_as_float(zk[m][0] & 0xffff0000u),
+                          __uint_as_float(zk[m][1] << 16), __uint_as_float(zk[m][1] & 0xffff0000u)};
+        f32x4 y;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) y[i] = wg[i] * (ok[m][i] * r) * silu_f(zf[i]);
+        bad |= lr < len - 16 * m &&
+               !(__builtin_isfinite(y[0]) && __builtin_isfinite(y[1]) && __builtin_isfinite(y[2]) && __builtin_isfinite(y[3]));
+        store_o4<OBF16>(ro, (((16 * m + lr) * H_v + h) * d_v + c0) * esz, y);
+      }
+    };
     auto step = [&](int it) {
       const int c = c_begin + it;
       const WideStage &P = sm.st[it & 1];
@@ -1017,132 +1059,77 @@ __global__ __launch_bounds__(64 * (kWideWaves + 1)) void wide_kernel(
                                                     (((16 * m + 4 * lg + i) * H_v + h) * d_v + cc[t]) * 4, 0, 0);
             }
       }
+      if constexpr (GATED) finish(it - 1, it > 0);  // the previous chunk's normed output
       // The output first (its registers are free again for the state update):
-      // o = diag(e^G rq) Q S + P U for these tiles, stored rows t0 .. t0 + len.
+      // o = diag(e^G rq) Q S + P U for these tiles, as its transpose (S^T Q^T + U^T P^T:
+      // the same fragments with the MFMA operands swapped), so that lane (g, l%16) holds
+      // token 16m + l%16 at the tile's columns 4g .. 4g + 3.
+      u32x4 pu_h[kTPW][2], pu_l[kTPW][2];
+#pragma unroll
+      for (int t = 0; t < kTPW; ++t) {
+        split8h(uacc[t][0], uacc[t][1], pu_h[t][0], pu_l[t][0]);
+        split8h(uacc[t][2], uacc[t][3], pu_h[t][1], pu_l[t][1]);
+      }
+      f32x4 ot[kTPW][4];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+#pragma unroll
+        for (int t = 0; t < kTPW; ++t) ot[t][m] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const u32x4 qf = P.qf[4 * m + s][fs];
+#pragma unroll
+          for (int t = 0; t < kTPW; ++t) ot[t][m] = mfma_h(sb[t][s], qf, ot[t][m]);
+        }
+        const float eq = P.fac[FAC_EQR][16 * m + lr];
+#pragma unroll
+        for (int t = 0; t < kTPW; ++t) ot[t][m] = ot[t][m] * eq;
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          if (s == 0 || m >= 2) {
+            const int f = 2 * tri_frag(m, s);
+            const u32x4 ph = P.pf[f][lane], pl = P.pf[f + 1][lane];
+#pragma unroll
+            for (int t = 0; t < kTPW; ++t) {
+              ot[t][m] = mfma_h(pu_h[t][s], ph, ot[t][m]);
+              ot[t][m] = mfma_h(pu_l[t][s], ph, ot[t][m]);
+              ot[t][m] = mfma_h(pu_h[t][s], pl, ot[t][m]);
+            }
+          }
+        }
+      }
       if constexpr (GATED) {
-        static_assert(kTPW == 1, "the gated output is written for one tile per wave");
-        // the gate z of this tile: rows 16m + l%16, columns 16 jt + 4g .. + 3 (bf16)
-        u32x2 zr[4];
-        {
-          const auto rz = rows_rsrc(const_cast<uint16_t *>(zg) + (int64_t)t0 * H_v * d_v, (int64_t)len * H_v * d_v * 2);
-#pragma unroll
-          for (int m = 0; m < 4; ++m)
-            zr[m] = __builtin_bit_cast(
-                u32x2, __builtin_amdgcn_raw_buffer_load_b64(rz, (((16 * m + lr) * H_v + h) * d_v + cc[0] - lr + 4 * lg) * 2,
-                                                            0, 0));
-        }
-        u32x4 pu_h[2], pu_l[2];
-        split8h(uacc[0][0], uacc[0][1], pu_h[0], pu_l[0]);
-        split8h(uacc[0][2], uacc[0][3], pu_h[1], pu_l[1]);
-        f32x4 oa[4];
+        static_assert(kTPW == 1, "the gated output is kept for one tile per wave");
+        // Kept for the norm after this step's closing barrier: o (ot), the gate z of the
+        // same elements, and this tile's share of each token's sum of squares in
+        // red[it % 2][token][tile] -- summed over the lane's 4 columns, then over the 4
+        // lane groups (lanes l, l ^ 16, l ^ 32); lane (g, l%16) writes token 16g + l%16.
+        const auto rz = rows_rsrc(const_cast<uint16_t *>(zg) + (int64_t)t0 * H_v * d_v, (int64_t)len * H_v * d_v * 2);
+        f32x4 sq;
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
-          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int s = 0; s < 4; ++s) acc = mfma_h(P.qf[4 * m + s][fs], sb[0][s], acc);
-          acc = acc * *reinterpret_cast<const f32x4 *>(&P.fac[FAC_EQR][16 * m + 4 * lg]);
-#pragma unroll
-          for (int s = 0; s < 2; ++s) {
-            if (s == 0 || m >= 2) {
-              const int f = 2 * tri_frag(m, s);
-              acc = mfma_h(P.pf[f][lane], pu_h[s], acc);
-              acc = mfma_h(P.pf[f][lane], pu_l[s], acc);
-              acc = mfma_h(P.pf[f + 1][lane], pu_h[s], acc);
-            }
-          }
-          oa[m] = acc;
+          zk[m] = __builtin_bit_cast(
+              u32x2, __builtin_amdgcn_raw_buffer_load_b64(rz, (((16 * m + lr) * H_v + h) * d_v + c0) * 2, 0, 0));
+          ok[m] = ot[0][m];
+          sq[m] = ot[0][m][0] * ot[0][m][0] + ot[0][m][1] * ot[0][m][1] + ot[0][m][2] * ot[0][m][2] +
+                  ot[0][m][3] * ot[0][m][3];
         }
-        // this tile's share of each token's sum of squares (row 16m + 4g + i), then the
-        // head's total from all tiles' shares
-        const int rb = it & 1;
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          f32x4 ps;
+        for (int m = 0; m < 4; ++m) sq[m] += lane_read(sq[m], lane ^ 16);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) ps[i] = row16_sum(oa[m][i] * oa[m][i]);
-          if (lr == 0) *reinterpret_cast<f32x4 *>(&sm.red[rb][kTPW * wave][16 * m + 4 * lg]) = ps;
-        }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-        if (lane == 0) __hip_atomic_fetch_add(&sm.cnt[rb], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-        const int target = kWideWaves * ((it >> 1) + 1);
-        for (int spins = 0; __hip_atomic_load(&sm.cnt[rb], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < target;) {
-          if (++spins > kSpinLimit) {
-            late = true;
-            break;
-          }
-          __builtin_amdgcn_s_sleep(1);
-        }
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-        const auto ro = rows_rsrc(o ? static_cast<unsigned char *>(o) + (int64_t)t0 * H_v * d_v * esz : nullptr,
-                                  o ? (int64_t)len * H_v * d_v * esz : 0);
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          f32x4 tot = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int jj = 0; jj < kWideCols; ++jj) tot += *reinterpret_cast<const f32x4 *>(&sm.red[rb][jj][16 * m + 4 * lg]);
-          const f32x4 zz = mfma_bf16(__builtin_bit_cast(bf16x8, u32x4{zr[m][0], zr[m][1], 0u, 0u}),
-                                     __builtin_bit_cast(bf16x8, vsel), f32x4{0.f, 0.f, 0.f, 0.f});
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float rs = rsqrtf(tot[i] * (1.0f / d_v) + eps);
-            const float xv = wcol * (oa[m][i] * rs) * silu_f(zz[i]);
-            bad |= 16 * m + 4 * lg + i < len && !__builtin_isfinite(xv);
-            const int off = (((16 * m + 4 * lg + i) * H_v + h) * d_v + cc[0]) * esz;
-            if constexpr (OBF16)
-              __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(pk_bf16(xv, 0.f) & 0xffffu), ro, off, 0, 0);
-            else
-              __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(xv), ro, off, 0, 0);
-          }
-        }
+        for (int m = 0; m < 4; ++m) sq[m] += lane_read(sq[m], lane ^ 32);
+        sm.red[it & 1][lane][wave] = lg == 0 ? sq[0] : lg == 1 ? sq[1] : lg == 2 ? sq[2] : sq[3];
       } else {
-        u32x4 pu_h[kTPW][2], pu_l[kTPW][2];
-#pragma unroll
-        for (int t = 0; t < kTPW; ++t) {
-          split8h(uacc[t][0], uacc[t][1], pu_h[t][0], pu_l[t][0]);
-          split8h(uacc[t][2], uacc[t][3], pu_h[t][1], pu_l[t][1]);
-        }
         const auto ro = rows_rsrc(o ? static_cast<unsigned char *>(o) + (int64_t)t0 * H_v * d_v * esz : nullptr,
                                   o ? (int64_t)len * H_v * d_v * esz : 0);
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          f32x4 acc[kTPW];
+        for (int t = 0; t < kTPW; ++t)
 #pragma unroll
-          for (int t = 0; t < kTPW; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int s = 0; s < 4; ++s) {
-            const u32x4 qf = P.qf[4 * m + s][fs];
-#pragma unroll
-            for (int t = 0; t < kTPW; ++t) acc[t] = mfma_h(qf, sb[t][s], acc[t]);
+          for (int m = 0; m < 4; ++m) {
+            bad |= lr < len - 16 * m && !(__builtin_isfinite(ot[t][m][0]) && __builtin_isfinite(ot[t][m][1]) &&
+                                            __builtin_isfinite(ot[t][m][2]) && __builtin_isfinite(ot[t][m][3]));
+            store_o4<OBF16>(ro, (((16 * m + lr) * H_v + h) * d_v + 16 * (kTPW * wave + t) + 4 * lg) * esz, ot[t][m]);
           }
-          const f32x4 eq = *reinterpret_cast<const f32x4 *>(&P.fac[FAC_EQR][16 * m + 4 * lg]);
-#pragma unroll
-          for (int t = 0; t < kTPW; ++t) acc[t] = acc[t] * eq;
-#pragma unroll
-          for (int s = 0; s < 2; ++s) {
-            if (s == 0 || m >= 2) {
-              const int f = 2 * tri_frag(m, s);
-              const u32x4 ph = P.pf[f][lane], pl = P.pf[f + 1][lane];
-#pragma unroll
-              for (int t = 0; t < kTPW; ++t) {
-                acc[t] = mfma_h(ph, pu_h[t][s], acc[t]);
-                acc[t] = mfma_h(ph, pu_l[t][s], acc[t]);
-                acc[t] = mfma_h(pl, pu_h[t][s], acc[t]);
-              }
-            }
-          }
-#pragma unroll
-          for (int t = 0; t < kTPW; ++t)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              bad |= 16 * m + 4 * lg + i < len && !__builtin_isfinite(acc[t][i]);
-              const int off = (((16 * m + 4 * lg + i) * H_v + h) * d_v + cc[t]) * esz;
-              const float xv = acc[t][i];
-              if constexpr (OBF16)
-                __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(pk_bf16(xv, 0.f) & 0xffffu), ro, off, 0, 0);
-              else
-                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(xv), ro, off, 0, 0);
-            }
-        }
       }
       // U'' = diag(e^{G_last - G} rk) U and S <- e^{G_last} S + K^T U''
       u32x4 uh[kTPW][2], ul[kTPW][2];
@@ -1184,6 +1171,9 @@ __global__ __launch_bounds__(64 * (kWideWaves + 1)) void wide_kernel(
     };
     lds_barrier();
     for (int it = 0; it < nit; ++it) step(it);
+    if constexpr (GATED) {
+      if (nit > 0) finish(nit - 1, true);
+    }
     if (fin) {
 #pragma unroll
       for (int t = 0; t < kTPW; ++t)
@@ -1200,7 +1190,6 @@ __global__ __launch_bounds__(64 * (kWideWaves + 1)) void wide_kernel(
 #pragma unroll
         for (int i = 0; i < 4; ++i) bad |= !__builtin_isfinite(S[t][mt][i]);
     if (__builtin_amdgcn_ballot_w64(bad) != 0 && lane == 0) atomicOr(status, 2);
-    if (__builtin_amdgcn_ballot_w64(late) != 0 && lane == 0) atomicOr(status, 4);
   } else {
     // ------------------------------ copy wave --------------------------------
     // K, Q, T~, P fragments, the factors and the v rows of chunk c into stage b: global

@@ -147,7 +147,7 @@ size_t gdn_chunk_fwd_workspace(const gdn_shape *s, int32_t num_seqs);
  * value head, over that head's d_v values,
  *     out = weight * o / sqrt(mean(o^2) + eps) * silu(z).
  *   Arguments as gdn_chunk_fwd's, with o replaced by
- *   z              [B, T, H_v, d_v]   dtype (the gate input)
+ *   z              [B, T, H_v, d_v]   dtype (the gate input), aligned to 4 elements
  *   weight         [d_v] float32, 16-byte aligned
  *   eps            >= 0
  *   out            [B, T, H_v, d_v]   o_dtype (written); must not overlap any input
@@ -157,11 +157,9 @@ size_t gdn_chunk_fwd_workspace(const gdn_shape *s, int32_t num_seqs);
  * count -- the norm is applied in the chain's output stage and o itself is never
  * written; elsewhere the chain writes o into `out` and the norm then runs in place
  * over it (one more pass over out and z; with a bf16 out, o is then rounded to bf16
- * before the norm reads it, so the result carries two roundings instead of one).  In the fused case the waves of a
- * workgroup exchange their shares of each token's sum of squares through LDS with a
- * bounded wait; a wait that exceeds its bound sets bit 2 (value 4) of the status word
- * at the start of the workspace (the results are then invalid).  Status bits 0 and 1
- * as for gdn_chunk_fwd.
+ * before the norm reads it, so the result carries two roundings instead of one).
+ * The status word at the start of the workspace is as for gdn_chunk_fwd (in the fused
+ * case its bit 1 flags a non-finite normed output instead of a non-finite o).
  */
 gdn_status gdn_chunk_fwd_gated(const gdn_shape *s, const void *q, const void *k,
                                const void *v, const float *g, const float *beta,
