@@ -510,18 +510,40 @@ template <int NB> struct ChainSmem {
   u32x4 sx[2][NB][4][64];  // S at the chunk start, B operand (d_k step s), fp16, double buffered
   f32x4 uf[2][NB][4][64];  // U of a chunk in accumulator order (column tile, token tile), fp32, double buffered
 };
+// With the per-token states each (column block) runs as kStateHalves blocks, one per
+// half of S's d_k rows, whose stream_waves(NB) stream waves step that half of the block's
+// 16 NB columns; stream wave w keeps the keys of its rows as pairs, kp[w][t][p] = fp16
+// {K[t][2p'], K[t][2p' + 1]} for its p-th pair p' (rows padded by 4 words).
+constexpr int kStateHalves = 2;
+__host__ __device__ constexpr int stream_waves(int NB) { return NB == 1 ? 2 : 4; }
+template <int NB> struct ChainSmemStates : ChainSmem<NB> {
+  static constexpr int SW = stream_waves(NB), PW = DK / kStateHalves / 2 / SW;  // waves, key pairs per wave
+  uint32_t kp[SW][C][PW + 4];
+};
 
-template <int NB, bool STATES, bool OBF16>
-__global__ __launch_bounds__(64 * (NB + 3)) void chain_kernel(
+// The per-token states, by mode SM: SM_WRITE writes what the stream kernel expands (each
+// chunk's start state into scw, the tokens' write vectors into uw); SM_STREAM streams them
+// here: stream_waves(NB) more waves step the block's columns of S token by token,
+// S <- e^{g_t} S + k_t u_t^T, from U as the carry publishes it, and store the state
+// after every selected token: tl = t_lo + j t_step < t_hi (tl the token's index in
+// its row of rowT tokens) to states[row * n_sel + j].
+enum { SM_NONE = 0, SM_WRITE = 1, SM_STREAM = 2 };
+template <int NB, int SM, bool OBF16>
+__global__ __launch_bounds__(64 * (NB + 3 + (SM == SM_STREAM ? stream_waves(NB) : 0))) void chain_kernel(
     const uint16_t *__restrict__ v, const float *__restrict__ s0, const Seqs sq, const unsigned char *__restrict__ tt,
     const unsigned char *__restrict__ kk, int32_t *__restrict__ status, void *__restrict__ o,
-    float *__restrict__ fin, float *__restrict__ uw, float *__restrict__ scw, int H_qk, int H_v, int d_v, int MC,
-    int groups) {
-  __shared__ ChainSmem<NB> sm;
+    float *__restrict__ fin, float *__restrict__ uw, float *__restrict__ scw, float *__restrict__ states, int H_qk,
+    int H_v, int d_v, int MC, int groups, int rowT, int t_lo, int t_hi, int t_step, int n_sel) {
+  constexpr bool STATES = SM == SM_STREAM;
+  __shared__ std::conditional_t<STATES, ChainSmemStates<NB>, ChainSmem<NB>> sm;
   if (sq.bad()) return;
   const int NCB = d_v / (16 * NB);
-  const int u = xcd_group_remap(blockIdx.x, NCB * (H_v / H_qk), groups);
-  if (u < 0) return;
+  // with the states, each column block runs once per half of S's rows (rh): both carry
+  // the state; the first writes o and the final state, each streams its half's states
+  constexpr int RH = STATES ? kStateHalves : 1;
+  const int u0 = xcd_group_remap(blockIdx.x, RH * NCB * (H_v / H_qk), groups);
+  if (u0 < 0) return;
+  const int rh = u0 % RH, u = u0 / RH;
   // packed sequences are taken longest first (the plan's order)
   const int jb = u % NCB, h = (u / NCB) % H_v, n = sq.by_length(u / (NCB * H_v));
   const int j = h / (H_v / H_qk);
@@ -556,11 +578,9 @@ __global__ __launch_bounds__(64 * (NB + 3)) void chain_kernel(
     }
     lds_barrier();
     for (int it = 0; it < nit; ++it) {
-      const int c = c_begin + it;
       const ChainStage<NB> &P = sm.st[it & 1];
-      const int t0 = s_begin + it * C;
-      const int len = min(C, s_end - t0);
-      if constexpr (STATES) {
+      const int c = c_begin + it;
+      if constexpr (SM == SM_WRITE) {
         // the state at the chunk start
 #pragma unroll
         for (int mt = 0; mt < 8; ++mt)
@@ -574,19 +594,24 @@ __global__ __launch_bounds__(64 * (NB + 3)) void chain_kernel(
       // fragments, where lane (g, 4e + q) of its group addresses token 32 st (+16) + 4g
       // + e at d_k 16 mt + 4q, i.e. K fragment 4(2 st (+1)) + mt/2, lane 4g + e + 16q,
       // half mt%2.
+      // (With the per-token states the store stream sets the pace: the fragments are
+      // read where they are used, leaving registers for more stream waves.)
+      auto ktr = [&](int mt, int st) {
+        const unsigned char *b = reinterpret_cast<const unsigned char *>(&P.kf[8 * st + (mt >> 1)][tslot]) + 8 * (mt & 1);
+        const u32x2 lo = lds_read_tr16(b), hi = lds_read_tr16(b + 4 * 64 * 16);
+        return u32x4{lo[0], lo[1], hi[0], hi[1]};
+      };
       u32x4 kfr[16];
-#pragma unroll
-      for (int f = 0; f < 16; ++f) kfr[f] = P.kf[f][pl];
       u32x4 ktf[8][2];
+      if constexpr (!STATES) {
 #pragma unroll
-      for (int mt = 0; mt < 8; ++mt)
+        for (int f = 0; f < 16; ++f) kfr[f] = P.kf[f][pl];
 #pragma unroll
-        for (int st = 0; st < 2; ++st) {
-          const unsigned char *b = reinterpret_cast<const unsigned char *>(&P.kf[8 * st + (mt >> 1)][tslot]) + 8 * (mt & 1);
-          const u32x2 lo = lds_read_tr16(b), hi = lds_read_tr16(b + 4 * 64 * 16);
-          ktf[mt][st] = u32x4{lo[0], lo[1], hi[0], hi[1]};
-        }
-      __builtin_amdgcn_sched_barrier(0);
+        for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+          for (int st = 0; st < 2; ++st) ktf[mt][st] = ktr(mt, st);
+        __builtin_amdgcn_sched_barrier(0);
+      }
       // K S: token tile m, four d_k steps
       f32x4 ks[4];
 #pragma unroll
@@ -594,7 +619,7 @@ __global__ __launch_bounds__(64 * (NB + 3)) void chain_kernel(
 #pragma unroll
       for (int s = 0; s < 4; ++s)
 #pragma unroll
-        for (int m = 0; m < 4; ++m) ks[m] = mfma_h(kfr[4 * m + s], sb[s], ks[m]);
+        for (int m = 0; m < 4; ++m) ks[m] = mfma_h(STATES ? P.kf[4 * m + s][pl] : kfr[4 * m + s], sb[s], ks[m]);
       // X = V - diag(e^G rk) K S
       f32x4 x[4];
 #pragma unroll
@@ -621,20 +646,20 @@ __global__ __launch_bounds__(64 * (NB + 3)) void chain_kernel(
         }
         uacc[m] = a;
       }
-      // publish U (fp32) for the output waves' next iteration
+      // publish U (fp32) for the output (and stream) waves' next iteration
 #pragma unroll
       for (int m = 0; m < 4; ++m) sm.uf[it & 1][jt][m][lane] = uacc[m];
-      if constexpr (STATES) {
+      if constexpr (SM == SM_WRITE) {
         // the tokens' write vectors, rows t0 .. t0 + len
+        const int t0 = s_begin + it * C;
+        const int len = min(C, s_end - t0);
         const auto rs = rows_rsrc(uw + (int64_t)t0 * H_v * d_v, (int64_t)len * H_v * d_v * 4);
 #pragma unroll
         for (int m = 0; m < 4; ++m)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float xv = uacc[m][i];
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(xv), rs,
+          for (int i = 0; i < 4; ++i)
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(uacc[m][i]), rs,
                                                   (((16 * m + 4 * lg + i) * H_v + h) * d_v + cc) * 4, 0, 0);
-          }
       }
       // U'' = diag(e^{G_last - G} rk) U as fp16 hi/lo
       f32x4 u2[4];
@@ -649,7 +674,7 @@ __global__ __launch_bounds__(64 * (NB + 3)) void chain_kernel(
       const float el = P.fac[FAC_EL][0];
 #pragma unroll
       for (int mt = 0; mt < 8; ++mt) {
-        const u32x4 k0 = ktf[mt][0], k1 = ktf[mt][1];
+        const u32x4 k0 = STATES ? ktr(mt, 0) : ktf[mt][0], k1 = STATES ? ktr(mt, 1) : ktf[mt][1];
         f32x4 a = S[mt] * el;
         a = mfma_h(k0, uh0, a);
         a = mfma_h(k0, ul0, a);
@@ -663,7 +688,7 @@ __global__ __launch_bounds__(64 * (NB + 3)) void chain_kernel(
       }
       lds_barrier();
     }
-    if (fin) {
+    if (fin && rh == 0) {
 #pragma unroll
       for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
@@ -774,10 +799,14 @@ __global__ __launch_bounds__(64 * (NB + 3)) void chain_kernel(
       }
       if (nit > 0) finish((nit - 1) & 1);
     };
-    if (wave == ROLE_OUT)
+    if (rh != 0) {  // o is the first row half's: here only the barriers
+      lds_barrier();
+      for (int it = 0; it < nit; ++it) lds_barrier();
+    } else if (wave == ROLE_OUT) {
       out_role(std::integral_constant<int, 0>{}, std::integral_constant<int, 3>{});
-    else
+    } else {
       out_role(std::integral_constant<int, 1>{}, std::integral_constant<int, 2>{});
+    }
     // rows past a chunk's length hold finite values that are never stored; a
     // non-finite stored row is what the range check reports
     if (__builtin_amdgcn_ballot_w64(bad) != 0 && lane == 0) atomicOr(status, 2);
@@ -853,6 +882,140 @@ __global__ __launch_bounds__(64 * (NB + 3)) void chain_kernel(
       if (it + 2 < nit) prep(0, c_begin + it + 2, va0, va1);
       lds_barrier();
     }
+  } else if constexpr (STATES) {
+    // ------------------------------ stream waves -----------------------------
+    // The block's 128 x 16 NB slice of S, in fp32, stepped through every token.  Lane
+    // l of stream wave w owns RPL consecutive rows at columns col0 + 4cq .. + 3 (cq =
+    // l % CQ), so that each store instruction writes whole 16 NB-column row segments
+    // (a 128-byte line at NB = 2).  Iteration it steps through chunk it - 1, with the
+    // U the carry published in the previous iteration (one chunk behind, as the output
+    // waves), then copies chunk it's keys (the stage's exact fp16 K fragments), decays
+    // e^{g_t} and key norms out of the stage: each wave into its own key region, so
+    // stepping and copying need no order between the waves.
+    constexpr int SW = stream_waves(NB), CQ = 4 * NB, RR = 64 / CQ, WR = DK / RH / SW, RPL = WR / RR;
+    static_assert(RPL % 2 == 0 && RPL <= 8 && WR % 16 == 0, "a lane's rows are whole key pairs");
+    const int sw = wave - (ROLE_COPY + 1);
+    const int cq = lane % CQ, rr = lane / CQ;
+    const int rb = DK / RH * rh + WR * sw;  // this wave's rows rb .. rb + WR
+    const int row0 = rb + RPL * rr;         // the lane's first row; its pairs start at pl0 in its wave's region
+    const int pl0 = RPL / 2 * rr;
+    f32x4 Sr[RPL];
+#pragma unroll
+    for (int e = 0; e < RPL; ++e) {
+      Sr[e] = s0 ? *reinterpret_cast<const f32x4 *>(s0 + ((int64_t)(n * H_v + h) * DK + row0 + e) * d_v + col0 + 4 * cq)
+                 : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    // e^{g_t} and rk_t of token t = lane: the chunk being copied and the one being stepped
+    float al_next = 0.f, rk_next = 0.f, al_cur = 0.f, rk_cur = 0.f;
+    auto capture = [&](int it) {
+      const ChainStage<NB> &P = sm.st[it & 1];
+      // this wave's rows rb .. rb + WR, 16 at a time (row block h16 = 2 st + half):
+      // lane (g, r) of fragment (m, st) holds token 16m + r at d_k 32st + 4g + i (words
+      // 0, 1) and 32st + 16 + 4g + i (words 2, 3), i.e. in words 2 half, 2 half + 1 the
+      // pairs of rows 16 h16 + 4g, 16 h16 + 4g + 2
+      const int r = lane & 15, g = lane >> 4;
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int hb = 0; hb < WR / 16; ++hb) {
+          const int h16 = rb / 16 + hb, st = h16 >> 1, half = h16 & 1;
+          const u32x4 x = P.kf[4 * m + st][kf_slot(lane)];
+          *reinterpret_cast<u32x2 *>(&sm.kp[sw][16 * m + r][8 * hb + 2 * g]) =
+              half ? u32x2{x[2], x[3]} : u32x2{x[0], x[1]};
+        }
+      // e^{g_t} as the difference of the cumulative decays (log2 e units), rk_t
+      const float gl = P.fac[FAC_GL2][lane], glp = lane > 0 ? P.fac[FAC_GL2][lane - 1] : 0.f;
+      al_next = __builtin_amdgcn_exp2f(gl - glp);
+      rk_next = P.fac[FAC_RK][lane];
+    };
+    const float *head0 = states + (int64_t)h * DK * d_v;
+    const int64_t sstride = (int64_t)H_v * DK * d_v;  // one token
+    const int off0 = (row0 * d_v + col0 + 4 * cq) * 4;
+    typedef uint32_t kpair_t __attribute__((ext_vector_type(RPL / 2)));
+    // one token: S <- e^{g_t} S + k_t u_t^T on this lane's rows (key pairs kw, fp16)
+    auto token = [&](int t, const f32x4 &uu, const kpair_t &kw) {
+      const float a = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, al_cur), t));
+      const float rkt = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, rk_cur), t));
+#pragma unroll
+      for (int e = 0; e < RPL; ++e) {
+        const uint32_t w = kw[e / 2];
+        const float ke = (float)__builtin_bit_cast(__fp16, (uint16_t)(e % 2 ? w >> 16 : w & 0xffffu)) * rkt;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) Sr[e][c] = __builtin_fmaf(Sr[e][c], a, ke * uu[c]);
+      }
+    };
+    auto store = [&](const float *dst) {
+      const auto rs = rows_rsrc(const_cast<float *>(dst), (int64_t)DK * d_v * 4);
+#pragma unroll
+      for (int e = 0; e < RPL; ++e)
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, Sr[e]), rs, off0 + e * d_v * 4, 0, 0);
+    };
+    // U of tokens 4tq .. 4tq + 3 at this lane's columns (token tile tq/4, lane group
+    // tq%4: u4[c][i] is token 4tq + i, column 4cq + c) and their key pairs
+    auto load4 = [&](int b, int tq, f32x4 (&u4)[4], kpair_t (&k4)[4]) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) u4[c] = sm.uf[b][cq >> 2][tq >> 2][16 * (tq & 3) + 4 * (cq & 3) + c];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) k4[i] = *reinterpret_cast<const kpair_t *>(&sm.kp[sw][4 * tq + i][pl0]);
+    };
+    auto step_tokens = [&](int it) {
+      const int b = it & 1;
+      const int t0 = s_begin + it * C;
+      const int len = min(C, s_end - t0);
+      // the chunk's tokens lie in one row: row brow, in-row indices tl0 .. tl0 + len;
+      // the next selected one is tl_sel = t_lo + j t_step (advanced as tokens pass, so
+      // the loop divides once per chunk)
+      const int brow = t0 / rowT, tl0 = t0 - brow * rowT;
+      int j = tl0 <= t_lo ? 0 : (tl0 - t_lo + t_step - 1) / t_step;
+      int tl_sel = t_lo + j * t_step;
+      const float *dst = head0 + ((int64_t)brow * n_sel + j) * sstride;  // state j's head block
+      // every token of a whole chunk kept: no test per token
+      const bool all = len == C && t_step == 1 && t_lo <= tl0 && tl0 + C <= t_hi;
+      auto group = [&](int tq, const f32x4 (&u4)[4], const kpair_t (&k4)[4]) {
+        if (all) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            token(4 * tq + i, f32x4{u4[0][i], u4[1][i], u4[2][i], u4[3][i]}, k4[i]);
+            store(dst);
+            dst += sstride;
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int t = 4 * tq + i;
+            if (t >= len) break;
+            token(t, f32x4{u4[0][i], u4[1][i], u4[2][i], u4[3][i]}, k4[i]);
+            if (tl0 + t == tl_sel && tl_sel < t_hi) {  // uniform over the block
+              store(dst);
+              dst += sstride;
+              tl_sel += t_step;
+            }
+          }
+        }
+      };
+      // two register sets, each loaded a group ahead of its use (plain arrays: a copy
+      // between them would wait for the loads)
+      const int ng = (len + 3) / 4;
+      f32x4 ua[4], ub[4];
+      kpair_t ka[4], kb[4];
+      load4(b, 0, ua, ka);
+      for (int tq = 0; tq < ng; tq += 2) {
+        if (tq + 1 < ng) load4(b, tq + 1, ub, kb);
+        group(tq, ua, ka);
+        if (tq + 1 >= ng) break;
+        if (tq + 2 < ng) load4(b, tq + 2, ua, ka);
+        group(tq + 1, ub, kb);
+      }
+    };
+    lds_barrier();
+    for (int it = 0; it < nit; ++it) {
+      if (it > 0) step_tokens(it - 1);
+      capture(it);  // after the step: the key region holds one chunk
+      al_cur = al_next;
+      rk_cur = rk_next;
+      lds_barrier();
+    }
+    if (nit > 0) step_tokens(nit - 1);
   }
 }
 
@@ -1246,15 +1409,17 @@ hipError_t launch_wide(const Problem &p, const ChunkArgs &a, const Seqs &sq, hip
   return hipGetLastError();
 }
 
-template <int NB, bool STATES, bool OBF16>
+template <int NB, int SM, bool OBF16>
 hipError_t launch_chain(const Problem &p, const ChunkArgs &a, const Seqs &sq, hipStream_t st) {
+  constexpr bool STATES = SM == SM_STREAM;
   const Workspace &w = a.ws;
   const int groups = p.N * p.H_qk, ncb = p.d_v / (16 * NB);
   if (groups == 0 || ncb == 0) return hipSuccess;
-  const int grid = xcd_group_grid(ncb * (p.H_v / p.H_qk), groups);
-  hipLaunchKernelGGL((chain_kernel<NB, STATES, OBF16>), dim3(grid), dim3(64 * (NB + 3)), 0, st,
-                     static_cast<const uint16_t *>(a.v), a.s0, sq, w.tt, w.kk, w.status, a.o, a.final_state, w.u,
-                     w.sc, p.H_qk, p.H_v, p.d_v, p.max_chunks, groups);
+  const int rowT = p.packed ? p.T_tot : p.T;
+  const int grid = xcd_group_grid((STATES ? kStateHalves : 1) * ncb * (p.H_v / p.H_qk), groups);
+  hipLaunchKernelGGL((chain_kernel<NB, SM, OBF16>), dim3(grid), dim3(64 * (NB + 3 + (STATES ? stream_waves(NB) : 0))),
+                     0, st, static_cast<const uint16_t *>(a.v), a.s0, sq, w.tt, w.kk, w.status, a.o, a.final_state,
+                     w.u, w.sc, a.states, p.H_qk, p.H_v, p.d_v, p.max_chunks, groups, rowT, a.t_lo, a.t_hi, a.t_step, a.n_sel);
   return hipGetLastError();
 }
 
@@ -1295,21 +1460,32 @@ hipError_t run_fused(const Problem &p, const ChunkArgs &a, hipStream_t st) {
   // A whole value head per workgroup once sequences x value heads fill every CU;
   // else two column tiles per workgroup (their carries share the stage and P) once
   // the single-tile grid would fill every CU twice over; one below that.
+  // The per-token states: streamed by the chain itself when at least half of each row's
+  // tokens are kept (32-column blocks where d_v allows, whose state rows are whole
+  // 128-byte lines); else, and behind the head-wide chain, the chain writes the chunk-start
+  // states and write vectors and the stream kernel expands only the chunks and tokens
+  // that the selection needs.
   const long blocks1 = (long)p.N * p.H_v * (p.d_v / 16);
-  if (fused_wide(p)) {
+  const bool wide = fused_wide(p);
+  const bool in_chain = STATES && !wide && 2L * a.n_sel >= (p.packed ? p.T_tot : p.T);
+  const bool two = p.d_v % 32 == 0 && (in_chain || blocks1 >= 2L * cu_count());
+  if (wide) {
     if (!STATES && a.z)
       e = launch_wide<false, OBF16, true>(p, a, sq, st);
     else
       e = launch_wide<STATES, OBF16, false>(p, a, sq, st);
+  } else if constexpr (STATES) {
+    if (in_chain)
+      e = two ? launch_chain<2, SM_STREAM, OBF16>(p, a, sq, st) : launch_chain<1, SM_STREAM, OBF16>(p, a, sq, st);
+    else
+      e = two ? launch_chain<2, SM_WRITE, OBF16>(p, a, sq, st) : launch_chain<1, SM_WRITE, OBF16>(p, a, sq, st);
+  } else {
+    e = two ? launch_chain<2, SM_NONE, OBF16>(p, a, sq, st) : launch_chain<1, SM_NONE, OBF16>(p, a, sq, st);
   }
-  else if (p.d_v % 32 == 0 && blocks1 >= 2L * cu_count())
-    e = launch_chain<2, STATES, OBF16>(p, a, sq, st);
-  else
-    e = launch_chain<1, STATES, OBF16>(p, a, sq, st);
   if (e != hipSuccess) return e;
   mark_event(a, 3, st);
   if constexpr (STATES) {
-    if ((e = launch_states_stream(p, a, sq, st)) != hipSuccess) return e;
+    if (!in_chain && (e = launch_states_stream(p, a, sq, st)) != hipSuccess) return e;
     mark_event(a, 4, st);
   }
   return hipSuccess;
