@@ -172,7 +172,7 @@ def test_states_t2048():
 
 def test_states_t2048_strided():
     """The states workload read at one state per 64-token chunk and over a token range: the
-    selected states against the oracle (sampled heads) and bit-identical to the full readout's."""
+    selected states against the oracle (sampled heads), the last one against the final state."""
     gdn = _gdn()
     inp = synth.make_inputs(synth.WORKLOADS["states_t2048"], seed=0)
     d = to_dev(inp)

@@ -321,8 +321,11 @@ def test_strided_states_fp32_and_bf16():
                                           t_begin=t0, t_end=t1, t_step=step)
         torch.cuda.synchronize()
         assert rel_fro(host(st[:, :, heads]), ref["states"][:, t0:t1:step]) <= TOL_BF16_STATE
-        # the same kernels as the full readout: the kept states are its states, bit for bit
-        assert torch.equal(st, st_all[:, t0:t1:step])
+        # A selection keeping under half of the tokens is expanded from the chunk-start
+        # states; the full readout is streamed by the chain from the initial state: two
+        # fp32 orders of the same recurrence, equal up to rounding.  o and the final state
+        # come from the same chain arithmetic: bit for bit.
+        assert rel_fro(host(st), host(st_all[:, t0:t1:step])) <= 1e-5
         assert torch.equal(o2, o) and torch.equal(fin2, fin)
 
 
