@@ -290,7 +290,20 @@ def bench_next_rows(lib, b, synth, to_dev, dev, torch, np):
             raise RuntimeError(lib.gdn_last_error().decode())
     ms = timed_launches(prologue, 51, 6, torch)
     pbytes = T * C * 2 + C * 4 * 4 + 2 * T * w.H_v * 4 + T * C * 2 + 2 * T * w.H_v * 4
+    # the same bytes moved by the runtime's device copy (half read, half written), over
+    # as many rotated buffers: what a plain stream of this size reaches on this GPU
+    csets = [(torch.empty(pbytes // 2, dtype=torch.uint8, device=dev),
+              torch.empty(pbytes // 2, dtype=torch.uint8, device=dev)) for _ in range(N_SETS)]
+
+    def copy_same():
+        src, dst = csets[turn[0] % N_SETS]
+        turn[0] += 1
+        dst.copy_(src)
+    ms_copy = timed_launches(copy_same, 51, 6, torch)
+    del csets
     out["prologue_t4096"] = {"us_per_call": round(ms * 1e3, 2), "input_sets_rotated": N_SETS,
+                             "device_copy_same_bytes_us": round(ms_copy * 1e3, 2),
+                             "device_copy_same_bytes_hbm_frac": round(pbytes / (ms_copy / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
                              "roofline": roofline("hbm", pbytes / (ms / 1e3) / 1e9, HBM_PEAK_GBS, "GB/s",
                                                   traffic=measured_traffic("conv_silu_kernel"),
                                                   kernel="conv_silu_kernel (gates in the same launch)",
