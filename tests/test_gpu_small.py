@@ -316,7 +316,10 @@ def test_strided_states_fp32_and_bf16():
     heads = [0, 13, 31]
     ref = _ref(inp, heads=heads, want_states=True)
     o, st_all, fin = gdn.gdn_states_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], initial_state=d["s0"])
-    for t0, t1, step in ((5, 150, 64), (37, 101, 1), (149, 150, 5)):
+    # the first three keep under half of each row's tokens (expanded from the chunk-start
+    # states), the last three at least half (streamed by the chain: a window that starts
+    # and ends inside chunks, and every second token)
+    for t0, t1, step in ((5, 150, 64), (37, 101, 1), (149, 150, 5), (20, 150, 1), (0, 140, 1), (0, 150, 2)):
         o2, st, fin2 = gdn.gdn_states_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], initial_state=d["s0"],
                                           t_begin=t0, t_end=t1, t_step=step)
         torch.cuda.synchronize()
@@ -337,12 +340,14 @@ def test_strided_states_packed_rows():
     d = to_dev(inp)
     heads = [2, 30]
     ref = _ref(inp, heads=heads, want_states=True)
-    t0, t1, step = 3, sum(lengths), 9
-    o, st, fin = gdn.gdn_states_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], initial_state=d["s0"],
-                                    cu_seqlens=d["cu"], t_begin=t0, t_end=t1, t_step=step)
-    torch.cuda.synchronize()
-    assert st.shape[:2] == (1, len(range(t0, t1, step)))
-    assert rel_fro(host(st[:, :, heads]), ref["states"][:, t0:t1:step]) <= TOL_BF16_STATE
+    # a sparse selection (expanded from the chunk-start states) and a dense one (streamed
+    # by the chain), both across sequence boundaries
+    for t0, t1, step in ((3, sum(lengths), 9), (3, sum(lengths) - 2, 1)):
+        o, st, fin = gdn.gdn_states_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], initial_state=d["s0"],
+                                        cu_seqlens=d["cu"], t_begin=t0, t_end=t1, t_step=step)
+        torch.cuda.synchronize()
+        assert st.shape[:2] == (1, len(range(t0, t1, step)))
+        assert rel_fro(host(st[:, :, heads]), ref["states"][:, t0:t1:step]) <= TOL_BF16_STATE
 
 
 @pytest.mark.parametrize("d_v", [32, 64, 96])
