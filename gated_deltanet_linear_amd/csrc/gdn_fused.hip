@@ -37,8 +37,15 @@
 //     output (2 waves)  form P from Q K^T and Q S for chunk c, and P U for chunk
 //                       c-1 (whose U the carry published before the last
 //                       barrier), and store o of chunk c-1: wave 0 token tiles
-//                       {0, 3}, wave 1 {1, 2}.
+//                       {0, 3}, wave 1 {1, 2};
+//     stream (with the states kept for at least half of the tokens) step the
+//                       block's columns of S through every token from the same
+//                       published U and store each kept state; each column block
+//                       then runs as two blocks, one per half of S's rows.
 //   One barrier per chunk, ordering LDS only; nothing else synchronises the waves.
+// wide chain (sequence, value head), where sequences x value heads fill every CU:
+//   eight column waves each carry one 16-column tile and form its output, with P
+//   from the solve; optionally with the mixer's output norm applied in place of o.
 //
 // MFMA lane order (v_mfma_f32_16x16x32_f16): lane l feeds row l%16 of A and
 // column l%16 of B, and 8 contraction indices chosen by the group g = l/16.
@@ -496,7 +503,8 @@ __global__ __launch_bounds__(256) void solve_kernel(const uint16_t *__restrict__
 
 // ---------------------------------------------------------------------------
 // chain: one (sequence, value head, block of 16 NB columns of S) per workgroup
-// of NB + 4 waves (see the head of the file).
+// of NB + 3 waves, and stream_waves(NB) more with the per-token states streamed here
+// (see the head of the file).
 // ---------------------------------------------------------------------------
 template <int NB> struct ChainStage {
   u32x4 kf[16][64];     // K, A operand of K S and K Q^T: fragment 4m + s, slot kf_slot(l) (copied)
@@ -1020,14 +1028,15 @@ __global__ __launch_bounds__(64 * (NB + 3 + (SM == SM_STREAM ? stream_waves(NB) 
 }
 
 // ---------------------------------------------------------------------------
-// wide chain: one (sequence, value head) per workgroup of 5 waves, for workloads
-// whose sequences x value heads fill every CU (d_v = 128).  Waves 0-3 each own two
-// 16-column tiles of S and run, for chunk c, both the carry (K S, X, T~ X, K^T U'')
-// and those tiles' output diag(e^G rq) Q S + P U from their own S and U registers,
-// each operand read from LDS serving both tiles; wave 4 copies chunk c + 1's K, Q,
-// T~, P (formed by the solve for these chains), factors and v rows into the other
-// LDS stage.  One barrier per chunk.  A head's eight tiles then run on the CU's
-// four MFMA units at once, where the narrow chain runs one or two carries per CU.
+// wide chain: one (sequence, value head) per workgroup of 9 waves, for workloads
+// whose sequences x value heads fill every CU (d_v = 128).  Waves 0-7 each own one
+// 16-column tile of S and run, for chunk c, both the carry (K S, X, T~ X, K^T U'')
+// and the tile's output diag(e^G rq) Q S + P U from their own S and U registers (the
+// output as its transpose, so that each lane stores four consecutive columns); wave 8
+// copies chunk c + 1's K, Q, T~, P (formed by the solve for these chains), factors and
+// v rows into the other LDS stage.  One barrier per chunk.  A chunk's fragments reach
+// LDS once for the whole head, where the narrow chain fetches them once per block of
+// columns.  With GATED the output norm is applied here (below).
 // ---------------------------------------------------------------------------
 constexpr int kWideCols = 8;                  // 16-column tiles of a head (d_v = 128)
 constexpr int kTPW = 1;                       // tiles per column wave
