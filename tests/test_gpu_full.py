@@ -189,3 +189,16 @@ def test_states_t2048_strided():
         if step == 64:
             assert rel_fro(host(st[:, -1]), host(fin)) <= 1e-5     # token 2047 is the last
         del o, st, fin
+
+
+def test_prefill_t32768_long_prompt():
+    """A 32768-token prompt (512 chunks in one carry) at the prefill's head shape, in the launch
+    configuration of the 4096-token one: sampled heads against the oracle, and every output finite."""
+    gdn = _gdn()
+    print("prefill T=32768, 16/32 heads, heads [2, 30]", flush=True)
+    inp = synth.make_inputs(synth.WORKLOADS["prefill_t4096"], seed=5, T=32768)
+    d = to_dev(inp)
+    o, fin = gdn.gdn_chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"])
+    torch.cuda.synchronize()
+    assert torch.isfinite(o).all() and torch.isfinite(fin).all()
+    _check_heads(o, fin, inp, [2, 30])
