@@ -219,8 +219,9 @@ gdn_status chunked_common(const gdn_shape *s, const void *q, const void *k, cons
   a.events = g_events;
   a.n_events = g_n_events;
   // The output norm runs inside the chain where one workgroup holds a whole value head
-  // (the head-wide chains); elsewhere it follows the chain, in place over o.
-  const bool fused_norm = gated && !with_states && p.dtype == GDN_BF16 && gdn::fused_wide(p);
+  // (the head-wide chains on dense rows; packed sequences split each head's columns
+  // over two workgroups); elsewhere it follows the chain, in place over o.
+  const bool fused_norm = gated && !with_states && p.dtype == GDN_BF16 && !p.packed && gdn::fused_wide(p);
   if (fused_norm) {
     a.z = z;
     a.nw = norm_w;

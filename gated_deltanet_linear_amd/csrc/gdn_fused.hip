@@ -1058,8 +1058,8 @@ struct WideSmem {
 // instead, the mean over the head's d_v values.  The tiles' waves leave their shares of
 // each chunk's sums of squares in LDS and finish the chunk's output after the barrier
 // that closes its step, so the sums need no wait of their own.
-template <bool STATES, bool OBF16, bool GATED>
-__global__ __launch_bounds__(64 * (kWideWaves + 1)) void wide_kernel(
+template <bool STATES, bool OBF16, bool GATED, int WC>
+__global__ __launch_bounds__(64 * (WC + 1)) void wide_kernel(
     const uint16_t *__restrict__ v, const float *__restrict__ s0, const Seqs sq, const unsigned char *__restrict__ tt,
     const unsigned char *__restrict__ kk, const unsigned char *__restrict__ pfw, int32_t *__restrict__ status,
     void *__restrict__ o, float *__restrict__ fin, float *__restrict__ uw, float *__restrict__ scw, int H_qk,
@@ -1067,9 +1067,13 @@ __global__ __launch_bounds__(64 * (kWideWaves + 1)) void wide_kernel(
   __shared__ WideSmem sm;
   if (sq.bad()) return;
   constexpr int d_v = 16 * kWideCols;
+  // WC column waves per block: the head's columns in NP parts (one block each, on one XCD)
+  constexpr int NP = kWideWaves / WC;
+  static_assert(NP * WC == kWideWaves && (!GATED || NP == 1), "the gated output needs the whole head in a block");
   // (sequence, query/key head) groups of H_v / H_qk value heads, longest sequences first
-  const int u = xcd_group_remap(blockIdx.x, H_v / H_qk, groups);
-  if (u < 0) return;
+  const int u0 = xcd_group_remap(blockIdx.x, NP * (H_v / H_qk), groups);
+  if (u0 < 0) return;
+  const int part = u0 % NP, u = u0 / NP;
   const int h = u % H_v, n = sq.by_length(u / H_v);
   const int j = h / (H_v / H_qk);
   const int lane = threadIdx.x & 63;
@@ -1080,15 +1084,16 @@ __global__ __launch_bounds__(64 * (kWideWaves + 1)) void wide_kernel(
   const int s_begin = sq.start(n), s_end = sq.start(n + 1);
   const int nit = c_end - c_begin;
 
-  if (wave < kWideWaves) {
+  if (wave < WC) {
     // ---------------------------- column waves -------------------------------
-    // Wave w owns the kTPW 16-column tiles jt = kTPW w + t; each operand read from LDS
-    // feeds all of them.
+    // Wave w owns the kTPW 16-column tiles jt = kTPW (WC part + w) + t; each operand read
+    // from LDS feeds all of them.
+    const int jw = WC * part + wave;
     const int tslot = kf_slot(4 * (lane >> 4) + ((lane >> 2) & 3) + 16 * (lane & 3));  // transposed-read slot
     const int64_t sbase = (int64_t)(n * H_v + h) * DK;
     int cc[kTPW];
 #pragma unroll
-    for (int t = 0; t < kTPW; ++t) cc[t] = 16 * (kTPW * wave + t) + lr;
+    for (int t = 0; t < kTPW; ++t) cc[t] = 16 * (kTPW * jw + t) + lr;
     f32x4 S[kTPW][8];  // S[t][mt]: rows 16 mt + 4g + i, column cc[t]
     u32x4 sb[kTPW][4];
 #pragma unroll
@@ -1115,7 +1120,7 @@ __global__ __launch_bounds__(64 * (kWideWaves + 1)) void wide_kernel(
     bool bad = false;
     // gated output: this lane's 4 columns of the tile, their gains, and the o and z of
     // the chunk whose output waits for the barrier that closed its step
-    const int c0 = 16 * kTPW * wave + 4 * lg;
+    const int c0 = 16 * kTPW * jw + 4 * lg;
     f32x4 wg = {0.f, 0.f, 0.f, 0.f};
     if constexpr (GATED) wg = *reinterpret_cast<const f32x4 *>(nw + c0);
     f32x4 ok[4] = {};
@@ -1181,7 +1186,7 @@ __global__ __launch_bounds__(64 * (kWideWaves + 1)) void wide_kernel(
       u32x4 xh[kTPW][2], xl[kTPW][2];
 #pragma unroll
       for (int t = 0; t < kTPW; ++t) {
-        const int jt = kTPW * wave + t;
+        const int jt = kTPW * jw + t;
         f32x4 x[4];
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
@@ -1300,7 +1305,7 @@ __global__ __launch_bounds__(64 * (kWideWaves + 1)) void wide_kernel(
           for (int m = 0; m < 4; ++m) {
             bad |= lr < len - 16 * m && !(__builtin_isfinite(ot[t][m][0]) && __builtin_isfinite(ot[t][m][1]) &&
                                             __builtin_isfinite(ot[t][m][2]) && __builtin_isfinite(ot[t][m][3]));
-            store_o4<OBF16>(ro, (((16 * m + lr) * H_v + h) * d_v + 16 * (kTPW * wave + t) + 4 * lg) * esz, ot[t][m]);
+            store_o4<OBF16>(ro, (((16 * m + lr) * H_v + h) * d_v + 16 * (kTPW * jw + t) + 4 * lg) * esz, ot[t][m]);
           }
       }
       // U'' = diag(e^{G_last - G} rk) U and S <- e^{G_last} S + K^T U''
@@ -1405,13 +1410,13 @@ __global__ __launch_bounds__(64 * (kWideWaves + 1)) void wide_kernel(
   }
 }
 
-template <bool STATES, bool OBF16, bool GATED>
+template <bool STATES, bool OBF16, bool GATED, int WC>
 hipError_t launch_wide(const Problem &p, const ChunkArgs &a, const Seqs &sq, hipStream_t st) {
   const Workspace &w = a.ws;
   const int groups = p.N * p.H_qk;
   if (groups == 0) return hipSuccess;
-  const int grid = xcd_group_grid(p.H_v / p.H_qk, groups);
-  hipLaunchKernelGGL((wide_kernel<STATES, OBF16, GATED>), dim3(grid), dim3(64 * (kWideWaves + 1)), 0, st,
+  const int grid = xcd_group_grid(kWideWaves / WC * (p.H_v / p.H_qk), groups);
+  hipLaunchKernelGGL((wide_kernel<STATES, OBF16, GATED, WC>), dim3(grid), dim3(64 * (WC + 1)), 0, st,
                      static_cast<const uint16_t *>(a.v), a.s0, sq, w.tt, w.kk, w.pf, w.status, a.o, a.final_state,
                      w.u, w.sc, p.H_qk, p.H_v, p.max_chunks, groups, static_cast<const uint16_t *>(a.z), a.nw,
                      a.eps);
@@ -1479,10 +1484,15 @@ hipError_t run_fused(const Problem &p, const ChunkArgs &a, hipStream_t st) {
   const bool in_chain = STATES && !wide && 2L * a.n_sel >= (p.packed ? p.T_tot : p.T);
   const bool two = p.d_v % 32 == 0 && (in_chain || blocks1 >= 2L * cu_count());
   if (wide) {
+    // Packed sequences of unequal lengths: each head in two blocks of half its columns,
+    // so that the longest sequences' chunks take about half as long (the norm needs the
+    // whole head in one block)
     if (!STATES && a.z)
-      e = launch_wide<false, OBF16, true>(p, a, sq, st);
+      e = launch_wide<false, OBF16, true, kWideWaves>(p, a, sq, st);
+    else if (p.packed)
+      e = launch_wide<STATES, OBF16, false, kWideWaves / 2>(p, a, sq, st);
     else
-      e = launch_wide<STATES, OBF16, false>(p, a, sq, st);
+      e = launch_wide<STATES, OBF16, false, kWideWaves>(p, a, sq, st);
   } else if constexpr (STATES) {
     if (in_chain)
       e = two ? launch_chain<2, SM_STREAM, OBF16>(p, a, sq, st) : launch_chain<1, SM_STREAM, OBF16>(p, a, sq, st);

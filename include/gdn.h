@@ -153,11 +153,13 @@ size_t gdn_chunk_fwd_workspace(const gdn_shape *s, int32_t num_seqs);
  *   out            [B, T, H_v, d_v]   o_dtype (written); must not overlap any input
  *   d_v must be one of 16, 32, 64, 128, 256 (the norm's widths).
  * Where the chain runs one workgroup per (sequence, value head) -- bf16 inputs at
- * chunk 64 with d_v = 128 once sequences x value heads reach the GPU's compute-unit
- * count -- the norm is applied in the chain's output stage and o itself is never
- * written; elsewhere the chain writes o into `out` and the norm then runs in place
- * over it (one more pass over out and z; with a bf16 out, o is then rounded to bf16
- * before the norm reads it, so the result carries two roundings instead of one).
+ * chunk 64 with d_v = 128 in dense rows (no cu_seqlens) once sequences x value heads
+ * reach the GPU's compute-unit count -- the norm is applied in the chain's output
+ * stage and o itself is never written.  Elsewhere (packed sequences there split each
+ * head's columns over two workgroups) the chain writes o into `out` and the norm then
+ * runs in place over it (one more pass over out and z; with a bf16 out, o is then
+ * rounded to bf16 before the norm reads it, so the result carries two roundings
+ * instead of one).
  * The status word at the start of the workspace is as for gdn_chunk_fwd (in the fused
  * case its bit 1 flags a non-finite normed output instead of a non-finite o).
  */

@@ -3,19 +3,22 @@ norm, out = weight * o / sqrt(mean(o^2) + eps) * silu(z) per (token, value head)
 the oracle composed the same way: mixer_ref.gated_rmsnorm(gdn_ref.recurrent(...)["o"], ...).
 
 Where the chain runs one workgroup per (sequence, value head) -- bf16 at chunk 64, d_v 128,
-sequences x value heads at least the compute-unit count (256 on an MI355X) -- the norm is
-applied in the chain's output stage and o never reaches memory: the 8-sequence packed
-workload at full size (sampled heads) and a 9-sequence packed case (all heads, both output
-dtypes).  Elsewhere the chain writes o and the norm runs in place over it: the 4096-token
-prefill (sampled heads), and small dense and fp32 cases (all heads).
+dense rows with sequences x value heads at least the compute-unit count (256 on an
+MI355X) -- the norm is applied in the chain's output stage and o never reaches memory:
+8 rows x 32 value heads (all heads, both output dtypes).  Elsewhere the chain writes o and
+the norm runs in place over it: packed sequences (whose heads the chain splits over two
+workgroups) at the 8-sequence workload's full size (sampled heads) and a 9-sequence case
+(all heads, both output dtypes), the 4096-token prefill (sampled heads), and small dense
+and fp32 cases (all heads).
 
 Tolerances: the fp32 output at the bf16 prompt path's 2e-2 x RMS, as for o (the norm rescales
 each row by its own RMS, so an error relative to the row's scale carries over), and checked
 inside 1e-2; the final state as for gdn_chunk_fwd; a bf16 output is the fp32 output of the
 same call rounded once where the norm is fused, and within three roundings where it follows
-the chain (o itself is then stored in bf16 before the norm reads it).  On the fused path the fp32 output also matches gdn_chunk_fwd
-followed by gdn_gated_norm on the GPU to 1e-5 (the same o; only the order of the sum of
-squares differs), and every call's status word is 0 (no bounded wait ran out).
+the chain (o itself is then stored in bf16 before the norm reads it).  In the all-heads
+cases the fp32 output also matches gdn_chunk_fwd followed by gdn_gated_norm on the GPU to
+1e-5 (the same o; only the order of the sum of squares may differ), and every call's
+status word is 0.
 """
 import dataclasses
 
@@ -93,15 +96,9 @@ def _check(inp, z, nw, heads=None, bf16_out=False, fused=True):
     return d, zd, wd, out
 
 
-def test_gated_packed_9seq_fused_all_heads():
-    """Nine packed sequences x 32 value heads: the head-wide chain with the norm inside."""
-    lens = (65, 1, 130, 0, 77, 64, 200, 33, 5)
-    w = synth.WORKLOADS["packed_8seq"]
-    print(f"packed lengths {lens}, fused norm, fp32 and bf16 out", flush=True)
-    inp = synth.make_inputs(w, seed=31, lengths=lens, s0_std=0.02)
-    z, nw = _gate(w, 32, inp)
-    d, zd, wd, out = _check(inp, z, nw, bf16_out=True)
-    # the same o through the unfused calls, then the norm on the GPU
+def _composition(d, zd, wd, out):
+    """The same o through gdn_chunk_fwd, then gdn_gated_norm on the GPU: within 1e-5 of the
+    gated call's fp32 output (only the order of the sum of squares may differ)."""
     gdn = _gdn()
     o, _ = gdn.gdn_chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], initial_state=d["s0"],
                              cu_seqlens=d["cu"])
@@ -110,9 +107,30 @@ def test_gated_packed_9seq_fused_all_heads():
     assert rel_max(host(out), host(comp)) <= 1e-5
 
 
+def test_gated_dense_wide_fused_all_heads():
+    """8 dense rows x 32 value heads: the head-wide chain with the norm inside."""
+    w = synth.WORKLOADS["packed_8seq"]
+    print("dense B=8 T=150, 32 value heads, fused norm, fp32 and bf16 out", flush=True)
+    inp = synth.make_inputs(w, seed=37, B=8, T=150, s0_std=0.02)
+    z, nw = _gate(w, 38, inp)
+    d, zd, wd, out = _check(inp, z, nw, bf16_out=True)
+    _composition(d, zd, wd, out)
+
+
+def test_gated_packed_9seq_all_heads():
+    """Nine packed sequences x 32 value heads: the split head-wide chain, then the norm."""
+    lens = (65, 1, 130, 0, 77, 64, 200, 33, 5)
+    w = synth.WORKLOADS["packed_8seq"]
+    print(f"packed lengths {lens}, norm after the chain, fp32 and bf16 out", flush=True)
+    inp = synth.make_inputs(w, seed=31, lengths=lens, s0_std=0.02)
+    z, nw = _gate(w, 32, inp)
+    d, zd, wd, out = _check(inp, z, nw, bf16_out=True, fused=False)
+    _composition(d, zd, wd, out)
+
+
 def test_gated_packed_8seq_full_size_sampled_heads():
     w = synth.WORKLOADS["packed_8seq"]
-    print(f"packed_8seq lengths {w.lengths}, fused norm, heads [5, 26]", flush=True)
+    print(f"packed_8seq lengths {w.lengths}, norm after the chain, heads [5, 26]", flush=True)
     inp = synth.make_inputs(w, seed=0)
     z, nw = _gate(w, 1, inp)
     _check(inp, z, nw, heads=[5, 26])

@@ -1,10 +1,12 @@
-"""GPU parity of the head-wide chain (one workgroup per sequence and value head, taken for bf16
-chunk-64 calls at d_v 128 once sequences x value heads reach the compute-unit count) in the
-cases the other tests leave out:
+"""GPU parity of the head-wide chain (taken for bf16 chunk-64 calls at d_v 128 once sequences
+x value heads reach the compute-unit count; one workgroup per sequence and value head on dense
+rows, two per head, each with half its columns, on packed sequences) in the cases the other
+tests leave out:
 
 - raw (un-normalised) keys and queries with the in-kernel l2 norm and no initial state, on the
-  plain, gated and per-token-states calls, every head;
-- more sequences than the plan kernel orders by length (4096), which then keeps their own order.
+  plain, gated and per-token-states calls, every head (packed: the split heads);
+- more sequences than the plan kernel orders by length (4096), which then keeps their own order;
+- dense rows (whole heads per workgroup): the plain and per-token-states calls, every head.
 
 Tolerances as for the bf16 prompt path: o (or the normed output) 2e-2 x RMS and inside 1e-2,
 final state and states 1e-3 relative.
@@ -86,3 +88,24 @@ def test_more_sequences_than_the_length_order_covers():
     # empty sequences hand their initial state straight through
     empty = [n for n, L in enumerate(lens) if L == 0][:5]
     assert torch.equal(fin[empty], d["s0"][empty])
+
+
+def test_wide_dense_rows_whole_heads():
+    gdn = _gdn()
+    print("dense B=8 T=150, 32 value heads (whole heads per workgroup), chunk and states", flush=True)
+    inp = synth.make_inputs(W, seed=45, B=8, T=150, s0_std=0.02)
+    d = to_dev(inp)
+    ref = gdn_ref.recurrent(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], s0=inp["s0"],
+                            want_states=True, heads=[1, 30])
+    full = gdn_ref.recurrent(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], s0=inp["s0"])
+    o, fin = gdn.gdn_chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], initial_state=d["s0"])
+    torch.cuda.synchronize()
+    eo, ef = rel_max(host(o), full["o"]), rel_fro(host(fin), full["final"])
+    print(f"  chunk: o {eo:.2e} final {ef:.2e}", flush=True)
+    assert eo <= TOL_BF16_O and eo <= 1e-2 and ef <= TOL_BF16_STATE
+    o2, st, fin2 = gdn.gdn_states_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], initial_state=d["s0"])
+    torch.cuda.synchronize()
+    es = rel_fro(host(st[:, :, [1, 30]]), ref["states"])
+    print(f"  states: {es:.2e}", flush=True)
+    assert es <= TOL_BF16_STATE
+    assert torch.equal(o2, o) and torch.equal(fin2, fin)
