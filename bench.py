@@ -526,7 +526,8 @@ def main():
             "kernel_us": {k: round(v * 1e3, 2) for k, v in zip(["plan", "solve", "chain"], kp_)},
             "roofline": roofline("mfma", cflop_p / (kp_[2] / 1e3) / 1e12, MFMA_BF16_PEAK_TFLOPS, "TFLOP/s",
                                  traffic=measured_traffic("wide_kernel_packed"),
-                                 kernel="wide_kernel (one workgroup per sequence and value head)",
+                                 kernel="wide_kernel (two workgroups per sequence and value head, half "
+                                        "of its columns each)",
                                  mfma_frac=round(cflop_p / (kp_[2] / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)),
             "path_mfma_frac": round(flop_p / (msp / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
             "path_hbm_frac": round(bytes_p / (msp / 1e3) / 1e9 / HBM_PEAK_GBS, 4)}
