@@ -46,6 +46,7 @@
 // wide chain (sequence, value head), where sequences x value heads fill every CU:
 //   eight column waves each carry one 16-column tile and form its output, with P
 //   from the solve; optionally with the mixer's output norm applied in place of o.
+//   Packed sequences split each head over two workgroups of four column waves.
 //
 // MFMA lane order (v_mfma_f32_16x16x32_f16): lane l feeds row l%16 of A and
 // column l%16 of B, and 8 contraction indices chosen by the group g = l/16.
@@ -1028,15 +1029,17 @@ __global__ __launch_bounds__(64 * (NB + 3 + (SM == SM_STREAM ? stream_waves(NB) 
 }
 
 // ---------------------------------------------------------------------------
-// wide chain: one (sequence, value head) per workgroup of 9 waves, for workloads
-// whose sequences x value heads fill every CU (d_v = 128).  Waves 0-7 each own one
-// 16-column tile of S and run, for chunk c, both the carry (K S, X, T~ X, K^T U'')
-// and the tile's output diag(e^G rq) Q S + P U from their own S and U registers (the
-// output as its transpose, so that each lane stores four consecutive columns); wave 8
-// copies chunk c + 1's K, Q, T~, P (formed by the solve for these chains), factors and
-// v rows into the other LDS stage.  One barrier per chunk.  A chunk's fragments reach
-// LDS once for the whole head, where the narrow chain fetches them once per block of
-// columns.  With GATED the output norm is applied here (below).
+// wide chain: one (sequence, value head) per workgroup of WC + 1 waves (WC = 8), or,
+// for packed sequences of unequal lengths, two workgroups per head with half its
+// columns each (WC = 4), for workloads whose sequences x value heads fill every CU
+// (d_v = 128).  Column wave w owns one 16-column tile of S and runs, for chunk c,
+// both the carry (K S, X, T~ X, K^T U'') and the tile's output diag(e^G rq) Q S + P U
+// from its own S and U registers (the output as its transpose, so that each lane
+// stores four consecutive columns); wave WC copies chunk c + 1's K, Q, T~, P (formed
+// by the solve for these chains), factors and v rows into the other LDS stage.  One
+// barrier per chunk.  A chunk's fragments reach LDS once per workgroup, where the
+// narrow chain fetches them once per 16 or 32 columns.  With GATED (whole heads only)
+// the output norm is applied here (below).
 // ---------------------------------------------------------------------------
 constexpr int kWideCols = 8;                  // 16-column tiles of a head (d_v = 128)
 constexpr int kTPW = 1;                       // tiles per column wave

@@ -103,7 +103,8 @@ hipError_t launch_fused_path(const Problem &p, const ChunkArgs &a, bool states, 
 size_t fused_t_bytes();
 size_t fused_k_bytes();
 size_t fused_p_bytes();
-// True when the fused path runs one workgroup per (sequence, value head) for this problem.
+// True when the fused path runs the head-wide chains for this problem: one workgroup per
+// (sequence, value head), or two per head (half its columns each) for packed sequences.
 bool fused_wide(const Problem &p);
 
 // True when a chunked-path kernel is built for this problem.
