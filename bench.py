@@ -31,6 +31,10 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
 N_SETS = 3                      # independent input/output sets rotated per step (cold reads)
+# Calls timed per row of the longer workloads (packed, states): the fixed cost of a timed
+# region (the first launch after a synchronisation, the wake-up at its end) is ~0.1-0.2 ms,
+# so a few calls of ~1 ms would carry it into every call's figure
+NSTEPS_LONG = 20
 
 
 def log(msg):
@@ -40,8 +44,8 @@ def log(msg):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--headline-only", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
@@ -242,7 +246,7 @@ def bench_next_rows(lib, b, synth, to_dev, dev, torch, np):
     for H_v in (16, 48):
         w = dataclasses.replace(base, H_v=H_v)
         calls = [prepare_chunk(lib, b, to_dev(synth.make_inputs(w, seed=s))) for s in range(N_SETS)]
-        ms, kern = timed_chunk_calls(lib, calls, 12, 3, 3)
+        ms, kern = timed_chunk_calls(lib, calls, 40, 3, 3)
         flop, nbytes, cflop, cbytes = chunk_work(w.T, H_v)
         out[f"prefill_t4096_h16_{H_v}"] = {
             "H_qk": 16, "H_v": H_v, "us_per_call": round(ms * 1e3, 2),
@@ -263,10 +267,10 @@ def bench_next_rows(lib, b, synth, to_dev, dev, torch, np):
     del mi
     call8 = prepare_chunk(lib, b, d8)
     callg8 = prepare_chunk(lib, b, d8, gated=(z8, nw8))
-    _, kg8 = timed_chunk_calls(lib, [callg8], 8, 2, 3)
-    _, k8 = timed_chunk_calls(lib, [call8], 8, 2, 3)
+    _, kg8 = timed_chunk_calls(lib, [callg8], 20, 2, 3)
+    _, k8 = timed_chunk_calls(lib, [call8], 20, 2, 3)
     # both compositions timed the same way: back-to-back calls between two events
-    msg8 = timed_launches(callg8, 8, 2, torch)
+    msg8 = timed_launches(callg8, 20, 2, torch)
     o8 = call8.keep[0]
     sn8 = b.GdnShape(w8.B, w8.T, 1, w8.H_v, 1, w8.d_v, 1, 1.0, b.GDN_BF16, b.GDN_F32, 0)
     nargs8 = [P(o8), P(z8), P(nw8), ctypes.c_float(1e-6), P(o8), stream]
@@ -275,7 +279,7 @@ def bench_next_rows(lib, b, synth, to_dev, dev, torch, np):
         call8()
         if lib.gdn_gated_norm(ctypes.byref(sn8), *nargs8) != 0:
             raise RuntimeError(lib.gdn_last_error().decode())
-    msn8 = timed_launches(chunk_then_norm8, 8, 2, torch)
+    msn8 = timed_launches(chunk_then_norm8, 20, 2, torch)
     el8 = w8.B * w8.T * w8.H_v * w8.d_v
     out["gated_dense_b8_t4096"] = {
         "B": w8.B, "T": w8.T, "us_per_call_fused": round(msg8 * 1e3, 2),
@@ -518,7 +522,7 @@ def main():
         wp = synth.WORKLOADS["packed_8seq"]
         dp = to_dev(synth.make_inputs(wp, seed=0))
         callp = prepare_chunk(lib, b, dp)
-        msp, kp_ = timed_chunk_calls(lib, [callp], max(3, args.steps // 4), 2, 3)
+        msp, kp_ = timed_chunk_calls(lib, [callp], NSTEPS_LONG, 2, 3)
         flop_p, bytes_p, cflop_p, cbytes_p = chunk_work(wp.T, wp.H_v)
         result["packed"] = {
             "workload": "packed_8seq", "tokens": wp.T, "us_per_call": round(msp * 1e3, 2),
@@ -540,9 +544,9 @@ def main():
         nwp = torch.from_numpy(mi["norm_w"]).to(dev)
         del mi
         callg = prepare_chunk(lib, b, dp, gated=(zp, nwp))
-        _, kg_ = timed_chunk_calls(lib, [callg], max(3, args.steps // 4), 2, 3)
+        _, kg_ = timed_chunk_calls(lib, [callg], NSTEPS_LONG, 2, 3)
         # both compositions timed the same way: back-to-back calls between two events
-        msg = timed_launches(callg, max(3, args.steps // 4), 2, torch)
+        msg = timed_launches(callg, NSTEPS_LONG, 2, torch)
         op = callp.keep[0]
         sn = b.GdnShape(1, wp.T, 1, wp.H_v, 1, wp.d_v, 1, 1.0, b.GDN_BF16, b.GDN_F32, 0)
         nargs = [ctypes.c_void_p(op.data_ptr()), ctypes.c_void_p(zp.data_ptr()), ctypes.c_void_p(nwp.data_ptr()),
@@ -553,7 +557,7 @@ def main():
             callp()
             if lib.gdn_gated_norm(ctypes.byref(sn), *nargs) != 0:
                 raise RuntimeError(lib.gdn_last_error().decode())
-        msn = timed_launches(chunk_then_norm, max(3, args.steps // 4), 2, torch)
+        msn = timed_launches(chunk_then_norm, NSTEPS_LONG, 2, torch)
         result["packed"]["gated"] = {
             "us_per_call": round(msg * 1e3, 2),
             "kernel_us": {k: round(v * 1e3, 2) for k, v in zip(["plan", "solve", "chain"], kg_)},
@@ -567,7 +571,7 @@ def main():
         ws_ = synth.WORKLOADS["states_t2048"]
         dsx = to_dev(synth.make_inputs(ws_, seed=0))
         calls = prepare_chunk(lib, b, dsx, states=True)
-        mss, ks_ = timed_chunk_calls(lib, [calls], 5, 2, 4)
+        mss, ks_ = timed_chunk_calls(lib, [calls], NSTEPS_LONG, 2, 4)
         # every state is kept: the chain kernel streams them itself (no stream kernel runs);
         # its bytes are the states plus the path's q, k, v, g, beta and o
         sbytes = ws_.T * ws_.H_v * 128 * 128 * 4
@@ -586,7 +590,7 @@ def main():
         del calls
         # the same call keeping one state per 64-token chunk (the chunk-boundary states)
         callx = prepare_chunk(lib, b, dsx, states=True, select=(63, ws_.T, 64))
-        msx, kx_ = timed_chunk_calls(lib, [callx], 10, 3, 4)
+        msx, kx_ = timed_chunk_calls(lib, [callx], NSTEPS_LONG, 3, 4)
         result["states"]["strided_t_step_64"] = {
             "us_per_call": round(msx * 1e3, 2), "tokens_per_s": round(ws_.T / (msx / 1e3), 1),
             "states_kept": len(range(63, ws_.T, 64)),
