@@ -1488,8 +1488,8 @@ hipError_t run_fused(const Problem &p, const ChunkArgs &a, hipStream_t st) {
   const bool two = p.d_v % 32 == 0 && (in_chain || blocks1 >= 2L * cu_count());
   if (wide) {
     // Packed sequences of unequal lengths: each head in two blocks of half its columns,
-    // so that the longest sequences' chunks take about half as long (the norm needs the
-    // whole head in one block)
+    // so that a chunk of the longest sequences takes less time and the shorter
+    // sequences' blocks fill the CUs (the norm needs the whole head in one block)
     if (!STATES && a.z)
       e = launch_wide<false, OBF16, true, kWideWaves>(p, a, sq, st);
     else if (p.packed)
