@@ -1029,7 +1029,7 @@ Workspace workspace_layout(const Problem &p, bool states, void *base) {
   const size_t cc = (size_t)p.max_chunks * p.H_v;
   const bool fused = p.dtype == GDN_BF16 && p.C == 64;  // the path of gdn_fused.hip
   size_t tb = 0, pm = 0, eg = 0, eb = 0, tt = 0, kk = 0, pf = 0;
-  const bool wide = fused && fused_wide(p);
+  const bool wide = fused && fused_solve_p(p);  // the solve forms P for these chains
   if (fused) {
     tt = take(fused_t_bytes() * cc);
     kk = take(fused_k_bytes() * (size_t)p.max_chunks * p.H_qk);

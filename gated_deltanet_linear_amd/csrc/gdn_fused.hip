@@ -45,8 +45,9 @@
 //   One barrier per chunk, ordering LDS only; nothing else synchronises the waves.
 // wide chain (sequence, value head), where sequences x value heads fill every CU:
 //   eight column waves each carry one 16-column tile and form its output, with P
-//   from the solve; optionally with the mixer's output norm applied in place of o.
-//   Packed sequences split each head over two workgroups of four column waves.
+//   formed by the copy wave; optionally with the mixer's output norm applied in place
+//   of o.  Packed sequences split each head over two workgroups of four column waves,
+//   which take P from the solve.
 //
 // MFMA lane order (v_mfma_f32_16x16x32_f16): lane l feeds row l%16 of A and
 // column l%16 of B, and 8 contraction indices chosen by the group g = l/16.
@@ -196,7 +197,7 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const void *p) {
 constexpr size_t kTFragBytes = 2 * kTriFrags * 64 * 16;
 enum { FAC_GL2 = 0, FAC_EKR, FAC_FKR, FAC_EQR, FAC_RK, FAC_RQ, FAC_EL, kFacRows = 8 };
 constexpr size_t kTBytes = kTFragBytes + kFacRows * C * 4;
-// Per (value head, chunk), head-wide chains only: P's hi/lo A fragments, as T~'s.
+// Per (value head, chunk), split head-wide chains only: P's hi/lo A fragments, as T~'s.
 constexpr size_t kPBytes = 2 * kTriFrags * 64 * 16;
 // Per (query/key head, chunk): 16 K fragments, then 16 Q fragments (fp16).
 constexpr size_t kKFragBytes = 16 * 64 * 16;
@@ -235,7 +236,7 @@ __device__ __forceinline__ f32x4 block_mm_acc(const float *X, int ib, int m, con
   return acc;
 }
 
-template <bool WP>  // WP: also P's fragments, for head-wide chains
+template <bool WP>  // WP: also P's fragments, for split head-wide chains
 __global__ __launch_bounds__(256) void solve_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
                                                     const float *__restrict__ g, const float *__restrict__ beta,
                                                     const Seqs seqs, int32_t *__restrict__ status,
@@ -344,7 +345,7 @@ __global__ __launch_bounds__(256) void solve_kernel(const uint16_t *__restrict__
     }
     gt[qq] = a;
   }
-  // For head-wide chains, K Q^T for P: wave w takes query tile m = w, key tiles ni <= m:
+  // For split head-wide chains, K Q^T for P: wave w takes query tile m = w, key tiles ni <= m:
   // D(ni, m) holds, in lane l, query 16m + l%16 at keys 16ni + 4g + i, the A operand of
   // P U once the key tiles are paired (2s, 2s + 1).
   f32x4 gp[4];
@@ -472,7 +473,7 @@ __global__ __launch_bounds__(256) void solve_kernel(const uint16_t *__restrict__
       }
     }
     // P[r][i] = rq_r rk_i e^{G_r - G_i} (q_r . k_i), i <= r, as fp16 hi/lo A fragments
-    // (row tile m = w), for head-wide chains
+    // (row tile m = w), for split head-wide chains
     if constexpr (WP) {
       const int m = w, r = 16 * m + lr;
       const double gr = sm.gam[r];
@@ -1035,8 +1036,9 @@ __global__ __launch_bounds__(64 * (NB + 3 + (SM == SM_STREAM ? stream_waves(NB) 
 // (d_v = 128).  Column wave w owns one 16-column tile of S and runs, for chunk c,
 // both the carry (K S, X, T~ X, K^T U'') and the tile's output diag(e^G rq) Q S + P U
 // from its own S and U registers (the output as its transpose, so that each lane
-// stores four consecutive columns); wave WC copies chunk c + 1's K, Q, T~, P (formed
-// by the solve for these chains), factors and v rows into the other LDS stage.  One
+// stores four consecutive columns); wave WC copies chunk c + 1's K, Q, T~ fragments,
+// factors and v rows into the other LDS stage and, for whole heads, forms P from K and
+// Q there (for split heads the solve forms P and the wave copies it).  One
 // barrier per chunk.  A chunk's fragments reach LDS once per workgroup, where the
 // narrow chain fetches them once per 16 or 32 columns.  With GATED (whole heads only)
 // the output norm is applied here (below).
@@ -1073,6 +1075,9 @@ __global__ __launch_bounds__(64 * (WC + 1)) void wide_kernel(
   // WC column waves per block: the head's columns in NP parts (one block each, on one XCD)
   constexpr int NP = kWideWaves / WC;
   static_assert(NP * WC == kWideWaves && (!GATED || NP == 1), "the gated output needs the whole head in a block");
+  // P: formed by the copy wave where a block holds the whole head (its chunks are long enough
+  // to hide the work), else formed by the solve and copied
+  constexpr bool PIB = NP == 1;
   // (sequence, query/key head) groups of H_v / H_qk value heads, longest sequences first
   const int u0 = xcd_group_remap(blockIdx.x, NP * (H_v / H_qk), groups);
   if (u0 < 0) return;
@@ -1378,15 +1383,17 @@ __global__ __launch_bounds__(64 * (WC + 1)) void wide_kernel(
       WideStage &S = sm.st[b];
       const u32x4 *ksrc = reinterpret_cast<const u32x4 *>(kk + ((int64_t)j * MC + c) * kKBytes) + lane;
       const u32x4 *tsrc = reinterpret_cast<const u32x4 *>(tt + ((int64_t)h * MC + c) * kTBytes) + lane;
-      const u32x4 *psrc = reinterpret_cast<const u32x4 *>(pfw + ((int64_t)h * MC + c) * kPBytes) + lane;
 #pragma unroll
       for (int f = 0; f < 16; ++f) lds_copy16(ksrc + f * 64, &S.kf[f][0]);
 #pragma unroll
       for (int f = 0; f < 16; ++f) lds_copy16(ksrc + (16 + f) * 64, &S.qf[f][0]);
 #pragma unroll
       for (int f = 0; f < 2 * kTriFrags; ++f) lds_copy16(tsrc + f * 64, &S.tf[f][0]);
+      if constexpr (!PIB) {
+        const u32x4 *psrc = reinterpret_cast<const u32x4 *>(pfw + ((int64_t)h * MC + c) * kPBytes) + lane;
 #pragma unroll
-      for (int f = 0; f < 2 * kTriFrags; ++f) lds_copy16(psrc + f * 64, &S.pf[f][0]);
+        for (int f = 0; f < 2 * kTriFrags; ++f) lds_copy16(psrc + f * 64, &S.pf[f][0]);
+      }
       lds_copy16(tsrc + 2 * kTriFrags * 64, &S.fac[0][0]);
       lds_copy16(tsrc + (2 * kTriFrags + 1) * 64, &S.fac[4][0]);
       // v rows: instruction f, lane l -> row 4f + l/16, slot l%16, which holds the row's
@@ -1403,6 +1410,45 @@ __global__ __launch_bounds__(64 * (WC + 1)) void wide_kernel(
         }
       }
       wait_vm<0>();
+      if constexpr (!PIB) return;
+      // P of chunk c from its K and Q fragments (now in the stage): for query tile m, the Gram
+      // K_ni Q_m^T of key tiles ni <= m holds, in lane l, query row 16m + l%16 at keys 16ni +
+      // 4g + i; scaled by rq_r rk_i e^{G_r - G_i} (i <= r, else zero) it is, as fp16 hi/lo,
+      // the A operand of P U for key steps s <= m / 2
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const int r = 16 * m + lr;
+        const float gr = S.fac[FAC_GL2][r], rq = S.fac[FAC_RQ][r];
+        u32x4 qf[4];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) qf[s] = S.qf[4 * m + s][fs];
+        f32x4 d[4];
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni) {
+          d[ni] = f32x4{0.f, 0.f, 0.f, 0.f};
+          if (ni <= m) {
+#pragma unroll
+            for (int s = 0; s < 4; ++s) d[ni] = mfma_h(S.kf[4 * ni + s][fs], qf[s], d[ni]);
+            const f32x4 rkc = *reinterpret_cast<const f32x4 *>(&S.fac[FAC_RK][16 * ni + 4 * lg]);
+            const f32x4 gc = *reinterpret_cast<const f32x4 *>(&S.fac[FAC_GL2][16 * ni + 4 * lg]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int i = 16 * ni + 4 * lg + e;
+              d[ni][e] = i <= r ? rq * rkc[e] * __builtin_amdgcn_exp2f(gr - gc[e]) * d[ni][e] : 0.f;
+            }
+          }
+        }
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+          if (st <= (m >> 1)) {
+            u32x4 hi, lo;
+            split8h(d[2 * st], d[2 * st + 1], hi, lo);
+            const int f = tri_frag(m, st);
+            S.pf[2 * f][lane] = hi;
+            S.pf[2 * f + 1][lane] = lo;
+          }
+        }
+      }
     };
     if (nit > 0) prep(0, c_begin);
     lds_barrier();
@@ -1521,6 +1567,7 @@ bool fused_wide(const Problem &p) {
   return p.dtype == GDN_BF16 && p.C == C && p.d_k == DK && p.d_v == 16 * kWideCols &&
          (long)p.N * p.H_v >= cu_count();
 }
+bool fused_solve_p(const Problem &p) { return fused_wide(p) && p.packed; }
 size_t fused_k_bytes() { return kKBytes; }
 
 hipError_t launch_fused_path(const Problem &p, const ChunkArgs &a, bool states, hipStream_t st) {

@@ -39,7 +39,7 @@ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 //   tt          [H_v, max_chunks, fused_t_bytes()]   T diag(beta) (fp16 hi/lo) and
 //                                                    the chain's per-token factors
 //   kk          [H_qk, max_chunks, fused_k_bytes()]  K and Q (fp16)
-//   pf          [H_v, max_chunks, fused_p_bytes()]   P (fp16 hi/lo), head-wide chains only
+//   pf          [H_v, max_chunks, fused_p_bytes()]   P (fp16 hi/lo), split head-wide chains only
 //   (states path only)
 //   u           f32 [T_tot, H_v, d_v]        per-token write vectors
 //   sc          f32 [max_chunks, H_v, d_k, d_v]  state at each chunk start
@@ -51,7 +51,7 @@ struct Workspace {
   float *tb = nullptr, *pm = nullptr, *eg = nullptr, *eb = nullptr;
   unsigned char *tt = nullptr;  // fused bf16 path: T diag(beta) fragments and factors per (value head, chunk)
   unsigned char *kk = nullptr;  // fused bf16 path: key and query fragments per (query/key head, chunk)
-  unsigned char *pf = nullptr;  // fused bf16 path, head-wide chains: P fragments per (value head, chunk)
+  unsigned char *pf = nullptr;  // fused bf16 path, split head-wide chains: P fragments per (value head, chunk)
   float *u = nullptr, *sc = nullptr;
   size_t bytes = 0;
 };
@@ -106,6 +106,9 @@ size_t fused_p_bytes();
 // True when the fused path runs the head-wide chains for this problem: one workgroup per
 // (sequence, value head), or two per head (half its columns each) for packed sequences.
 bool fused_wide(const Problem &p);
+// True when the solve also forms P for the chain (the split head-wide chains); the whole-head
+// chains form it themselves.
+bool fused_solve_p(const Problem &p);
 
 // True when a chunked-path kernel is built for this problem.
 bool chunk_path_supported(const Problem &p);
