@@ -5,7 +5,8 @@ the oracle composed the same way: mixer_ref.gated_rmsnorm(gdn_ref.recurrent(...)
 Where the chain runs one workgroup per (sequence, value head) -- bf16 at chunk 64, d_v 128,
 dense rows with sequences x value heads at least the compute-unit count (256 on an
 MI355X) -- the norm is applied in the chain's output stage and o never reaches memory:
-8 rows x 32 value heads (all heads, both output dtypes).  Elsewhere the chain writes o and
+8 rows x 32 value heads (all heads, both output dtypes) and 8 rows of 4096 tokens (sampled
+heads, with the plain chunk call on them).  Elsewhere the chain writes o and
 the norm runs in place over it: packed sequences (whose heads the chain splits over two
 workgroups) at the 8-sequence workload's full size (sampled heads) and a 9-sequence case
 (all heads, both output dtypes), the 4096-token prefill (sampled heads), and small dense
@@ -115,6 +116,24 @@ def test_gated_dense_wide_fused_all_heads():
     z, nw = _gate(w, 38, inp)
     d, zd, wd, out = _check(inp, z, nw, bf16_out=True)
     _composition(d, zd, wd, out)
+
+
+def test_gated_dense_8x4096_fused_sampled_heads():
+    """8 dense rows of the prefill's shape (64 chunks per row, whole heads per workgroup, P
+    formed in the chain): the fused norm and the plain chunk call on sampled heads."""
+    w = synth.WORKLOADS["prefill_t4096"]
+    print("dense B=8 T=4096, fused norm, heads [6, 25]", flush=True)
+    inp = synth.make_inputs(w, seed=39, B=8)
+    z, nw = _gate(w, 40, inp)
+    d, _, _, _ = _check(inp, z, nw, heads=[6, 25])
+    gdn = _gdn()
+    o, fin = gdn.gdn_chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"])
+    torch.cuda.synchronize()
+    ref = gdn_ref.recurrent(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], heads=[6, 25])
+    eo = rel_max(host(o[..., [6, 25], :]), ref["o"][..., [6, 25], :])
+    ef = rel_fro(host(fin[:, [6, 25]]), ref["final"][:, [6, 25]])
+    print(f"  chunk: o {eo:.2e} final {ef:.2e}", flush=True)
+    assert eo <= TOL_BF16_O and eo <= 1e-2 and ef <= TOL_BF16_STATE
 
 
 def test_gated_packed_9seq_all_heads():
