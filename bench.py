@@ -108,6 +108,14 @@ class Prepared:
         if st != 0:
             raise RuntimeError(self.lib.gdn_last_error().decode())
 
+    def check_status(self):
+        """The int32 status word at the start of the workspace after the last call: 0, or
+        the call's results are invalid (bad cu_seqlens, an fp16 overflow, a late hand-over)."""
+        import torch
+        word = int(self.ws[:4].view(torch.int32).item())
+        if word != 0:
+            raise RuntimeError(f"status word {word} after the timed calls")
+
 
 def prepare_chunk(lib, b, d, states=False, select=None, gated=None):
     """Bind a gdn_chunk_fwd (or gdn_states_fwd) call on device inputs d; with states and
@@ -152,6 +160,7 @@ def prepare_chunk(lib, b, d, states=False, select=None, gated=None):
             fn = lib.gdn_chunk_fwd_gated
         keep = (o, fin, ws) + (gated or ())
     call = Prepared(lib, fn, s, args)
+    call.ws = ws
     call.keep = keep + (d,)   # the C call holds raw pointers: keep every tensor alive
     return call
 
@@ -183,6 +192,8 @@ def timed_chunk_calls(lib, calls, steps, warmup, n_kernels):
         calls[i % len(calls)]()
     torch.cuda.synchronize()
     lib.gdn_set_timing_events(None, 0)
+    for c in calls:
+        c.check_status()
     per_kernel = [sum(row[j].elapsed_time(row[j + 1]) for row in evs) / steps for j in range(n_kernels)]
     return (t1 - t0) * 1e3 / steps, per_kernel
 
@@ -271,6 +282,7 @@ def bench_next_rows(lib, b, synth, to_dev, dev, torch, np):
     _, k8 = timed_chunk_calls(lib, [call8], 20, 2, 3)
     # both compositions timed the same way: back-to-back calls between two events
     msg8 = timed_launches(callg8, 20, 2, torch)
+    callg8.check_status()
     o8 = call8.keep[0]
     sn8 = b.GdnShape(w8.B, w8.T, 1, w8.H_v, 1, w8.d_v, 1, 1.0, b.GDN_BF16, b.GDN_F32, 0)
     nargs8 = [P(o8), P(z8), P(nw8), ctypes.c_float(1e-6), P(o8), stream]
@@ -280,6 +292,7 @@ def bench_next_rows(lib, b, synth, to_dev, dev, torch, np):
         if lib.gdn_gated_norm(ctypes.byref(sn8), *nargs8) != 0:
             raise RuntimeError(lib.gdn_last_error().decode())
     msn8 = timed_launches(chunk_then_norm8, 20, 2, torch)
+    call8.check_status()
     el8 = w8.B * w8.T * w8.H_v * w8.d_v
     out["gated_dense_b8_t4096"] = {
         "B": w8.B, "T": w8.T, "us_per_call_fused": round(msg8 * 1e3, 2),
@@ -547,6 +560,7 @@ def main():
         _, kg_ = timed_chunk_calls(lib, [callg], NSTEPS_LONG, 2, 3)
         # both compositions timed the same way: back-to-back calls between two events
         msg = timed_launches(callg, NSTEPS_LONG, 2, torch)
+        callg.check_status()
         op = callp.keep[0]
         sn = b.GdnShape(1, wp.T, 1, wp.H_v, 1, wp.d_v, 1, 1.0, b.GDN_BF16, b.GDN_F32, 0)
         nargs = [ctypes.c_void_p(op.data_ptr()), ctypes.c_void_p(zp.data_ptr()), ctypes.c_void_p(nwp.data_ptr()),
@@ -558,6 +572,7 @@ def main():
             if lib.gdn_gated_norm(ctypes.byref(sn), *nargs) != 0:
                 raise RuntimeError(lib.gdn_last_error().decode())
         msn = timed_launches(chunk_then_norm, NSTEPS_LONG, 2, torch)
+        callp.check_status()
         result["packed"]["gated"] = {
             "us_per_call": round(msg * 1e3, 2),
             "kernel_us": {k: round(v * 1e3, 2) for k, v in zip(["plan", "solve", "chain"], kg_)},
