@@ -35,3 +35,14 @@ def test_chunk_work_per_token_and_head():
 def test_roofline_fraction():
     r = bench.roofline("hbm", 6400.0, 8000.0, "GB/s", traffic=123, kernel="k")
     assert r["frac"] == 0.8 and r["bound"] == "hbm" and r["traffic"] == 123 and r["kernel"] == "k"
+
+
+def test_status_word_check():
+    # a timed row fails when a call left a nonzero status word at the start of its workspace
+    import torch
+    call = bench.Prepared(None, None, None, [])
+    call.ws = torch.zeros(64, dtype=torch.uint8)
+    call.check_status()
+    call.ws[:4].view(torch.int32)[0] = 2
+    with pytest.raises(RuntimeError, match="status word 2"):
+        call.check_status()
