@@ -426,8 +426,9 @@ def gdn_mixer_prologue(x, conv_w, a, b, A_log, dt_bias, H_qk, d_k, H_v, d_v, con
 
 
 def plan_status(workspace: torch.Tensor) -> int:
-    """The device status word a chunked call leaves at the start of its workspace
-    (nonzero when the call's cu_seqlens were malformed and every kernel did nothing)."""
+    """The device status word a chunked call leaves at the start of its workspace: 0, or bit 0
+    when the call's cu_seqlens were malformed (every kernel then did nothing), bit 1 when a
+    stored o or final-state value of the bf16 chunk-64 path is not finite."""
     return int(workspace[:4].view(torch.int32).item())
 
 

@@ -110,7 +110,11 @@ typedef struct {
  *   q, k           [B, T, H_qk, d_k]  dtype
  *   v              [B, T, H_v, d_v]   dtype
  *   g, beta        [B, T, H_v]        float32; g is a log decay (<= 0, -inf
- *                                     resets the state), beta the write strength
+ *                                     resets the state; a NaN makes that head's
+ *                                     o and state non-finite from its token on,
+ *                                     on the bf16 chunk-64 path possibly from
+ *                                     earlier tokens of its chunk, and sets bit 1
+ *                                     of the status word), beta the write strength
  *   initial_state  [N, H_v, d_k, d_v] float32, or NULL for a zero state
  *   cu_seqlens     int32 [N+1] on the device, or NULL.  Non-NULL packs N
  *                  sequences on one row (B == 1): sequence n owns tokens

@@ -441,3 +441,37 @@ def test_bad_cu_seqlens_makes_the_call_a_noop():
     torch.cuda.synchronize()
     assert binding.plan_status(ws) != 0
     assert torch.all(o == 7.0)
+
+
+def test_nan_decay_propagates():
+    """A NaN decay at token t of one head reaches that head's o and state from t on (as in the
+    oracle's recurrence) and no other head.  The chunk form may also carry it to the earlier
+    tokens of t's chunk (a zero of T~ or P times a NaN row in one MFMA), so those tokens are
+    left unchecked; the chunks before it match the oracle, and the call sets bit 1 of the
+    status word."""
+    from gated_deltanet_linear_amd import binding
+    gdn = _lib()
+    inp = _bf16_case(T=150, seed=13, s0_std=0.02)
+    hn, tn = 7, 100                      # head 7, token 36 of the second chunk
+    inp["g"][0, tn, hn] = np.nan
+    d = to_dev(inp)
+    ref = _ref(inp)
+    assert np.isnan(ref["o"][0, tn:, hn]).all() and np.isfinite(ref["o"][0, :tn, hn]).all()
+    need = binding.gdn_chunk_fwd_workspace(binding._shape(d["q"], d["v"], None, None, False, torch.float32, 1, 150), 0)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    o, fin = gdn.gdn_chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], initial_state=d["s0"], workspace=ws)
+    o2, st, fin2 = gdn.gdn_states_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], initial_state=d["s0"])
+    torch.cuda.synchronize()
+    assert binding.plan_status(ws) & 2
+    others = [h for h in range(32) if h != hn]
+    oh, sth = host(o), host(st)
+    assert np.isfinite(oh[:, :, others]).all() and np.isfinite(host(fin)[:, others]).all()
+    assert rel_max(oh[:, :, others], ref["o"][:, :, others]) <= TOL_BF16_O
+    assert rel_fro(host(fin)[:, others], ref["final"][:, others]) <= TOL_BF16_STATE
+    # the NaN head: exact before t's chunk, non-finite from t on, in o, the states and the final state
+    assert rel_max(oh[:, :64, hn], ref["o"][:, :64, hn]) <= TOL_BF16_O
+    assert not np.isfinite(oh[0, tn:, hn]).any()
+    assert not np.isfinite(host(fin)[0, hn]).any()
+    assert np.isfinite(sth[0, :64, hn]).all() and not np.isfinite(sth[0, tn:, hn]).any()
+    assert torch.equal(o2, o) or np.array_equal(host(o2), oh, equal_nan=True)
+    assert np.array_equal(host(fin2), host(fin), equal_nan=True)
