@@ -885,7 +885,7 @@ __global__ __launch_bounds__(256) void stream_kernel(
                                 (int64_t)d_k * d_v * 4);
 #pragma unroll
       for (int i = 0; i < SRPT; ++i)
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, Sv[i]), rs, off0 + i * roff, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, Sv[i]), rs, off0 + i * roff, 0, 2);
     }
   }
 }

@@ -33,6 +33,15 @@ __device__ __forceinline__ void store4(uint16_t *p, const f32x4 &x) {
   *reinterpret_cast<u32x2 *>(p) = u32x2{(uint32_t)f2bf(x[0]) | ((uint32_t)f2bf(x[1]) << 16),
                                         (uint32_t)f2bf(x[2]) | ((uint32_t)f2bf(x[3]) << 16)};
 }
+// The same, non-temporal: a final output that nothing reads back soon.
+__device__ __forceinline__ void store4_nt(float *p, const f32x4 &x) {
+  __builtin_nontemporal_store(x, reinterpret_cast<f32x4 *>(p));
+}
+__device__ __forceinline__ void store4_nt(uint16_t *p, const f32x4 &x) {
+  __builtin_nontemporal_store(u32x2{(uint32_t)f2bf(x[0]) | ((uint32_t)f2bf(x[1]) << 16),
+                                    (uint32_t)f2bf(x[2]) | ((uint32_t)f2bf(x[3]) << 16)},
+                              reinterpret_cast<u32x2 *>(p));
+}
 // x sigmoid(x) with the hardware reciprocal (1 ulp): a division's exact rounding
 // buys nothing for values that are then stored as bf16 or compared at 1e-5.
 __device__ __forceinline__ float silu(float x) { return x * __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
@@ -62,7 +71,7 @@ __global__ __launch_bounds__(256) void gated_norm_kernel(const TY *__restrict__ 
   f32x4 o;
 #pragma unroll
   for (int i = 0; i < 4; ++i) o[i] = wv[i] * (yv[i] * rs) * silu(zv[i]);
-  store4(out + r * DV + c, o);
+  store4_nt(out + r * DV + c, o);
 }
 
 template <typename TY, typename TZ>
