@@ -288,8 +288,9 @@ __global__ __launch_bounds__(256) void solve_kernel(const uint16_t *__restrict__
     for (int i = 0; i < 4; ++i) {
       const int x = tid + 256 * i, r = min(x >> 4, len - 1), cv = x & 15;
       const int64_t off = ((int64_t)(t0 + r) * H_qk + j) * DK + cv * 8;
-      kv[i] = *reinterpret_cast<const u32x4 *>(k + off);
-      qv[i] = *reinterpret_cast<const u32x4 *>(q + off);
+      // read once: non-temporal, so that the L2 keeps this kernel's outputs for the chain
+      kv[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(k + off));
+      qv[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(q + off));
     }
     const u32x4 zero = {0u, 0u, 0u, 0u};
 #pragma unroll
